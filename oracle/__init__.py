@@ -1,0 +1,35 @@
+"""Plain CPU float64 oracle for packed varlen modality-RoPE attention.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this package.  The HIP library never
+calls it and shares no code with it.
+
+Every function is the plain definition of one step, written in float64 with
+NumPy.  Citations name the page and its section:
+  [P1] "生产环境下的音视频联合生成：MiniMax-H3 与 vLLM-Omni 架构解析"
+  [P3] "突破视频生成大模型的工程瓶颈"
+
+Steps and the passages they follow:
+  pack            [P1] section 三 (packed sequence, cu_seqlens, its worked example)
+  time_shift      [P3] long-video continuation, step 3 (RoPE global time alignment)
+  rope_angles,
+  apply_rope      [P1] section 三 (modality tags select RoPE frequencies) with
+                  RoFormer's adjacent-pair rotation (Su et al., 2021)
+  attention       [P1] section 三 (softmax normalised inside one sub-sequence,
+                  out-of-segment weight zero) and section 六 (rows past the
+                  last cu_seqlens entry take no part)
+  unpack          [P1] section 三 (output sliced by modality) and [P3]
+                  window-aligned SP (token order restored)
+
+Pinning (tests/test_oracle.py): the page's cu_seqlens example and exact zeros,
+brute force in pure Python, torch's float64 scaled_dot_product_attention per
+segment, closed forms (L = 1, Q = 0, constant V, identical keys), the complex
+form of RoPE, the relative-position identity, time-shift invariance, and
+key-permutation invariance.  No function here is "parity unpinned".
+"""
+from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
+                        attention, attention_rows, attention_weights, unpack, run,
+                        rope_qk)
+
+__all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
+           "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk"]

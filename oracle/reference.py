@@ -1,0 +1,206 @@
+"""float64 reference of the packed varlen modality-RoPE attention path.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).  Inputs are NumPy arrays;
+floating-point inputs are upcast exactly to float64 by the caller.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+TEXT, VIDEO, AUDIO = 0, 1, 2
+
+
+# ---------------------------------------------------------------------------
+# a1: pack  ([P1] section 三: rows concatenated into one 1-D sequence;
+#           cu_seqlens holds the start/end offset of every sub-sequence)
+# ---------------------------------------------------------------------------
+def pack(seg: np.ndarray, n_seg: int):
+    """Stable order by segment id.
+
+    Returns (cu_seqlens int32 [n_seg+1], perm int32 [n]) where perm[p] is the
+    source row placed at packed row p and segment k occupies packed rows
+    [cu[k], cu[k+1]).  Tokens of one segment keep their source order.
+    """
+    seg = np.asarray(seg, np.int64)
+    perm = np.argsort(seg, kind="stable").astype(np.int32)
+    counts = np.bincount(seg, minlength=n_seg)[:n_seg]
+    cu = np.zeros(n_seg + 1, np.int64)
+    cu[1:] = np.cumsum(counts)
+    return cu.astype(np.int32), perm
+
+
+# ---------------------------------------------------------------------------
+# a2: modality RoPE with the continuation time shift
+# ---------------------------------------------------------------------------
+def time_shift(s: float) -> float:
+    """[P3] continuation step 3: t_global = t_local + s * 40 / 24 (40 Hz audio
+    latent rate over 24 FPS video), fraction kept."""
+    return s * 40.0 / 24.0
+
+
+def rope_angles(tags, pos, rope, time_offset: float, D: int) -> np.ndarray:
+    """Rotation angle of every (token, channel pair): float64 [n, D/2].
+
+    Token i of modality m = tags[i] has time coordinate
+        tau = pos[i, 0] * time_scale_m + (shift_m ? time_shift(s) : 0)
+    and spatial coordinates h = pos[i, 1], w = pos[i, 2].  The head dim is cut
+    into consecutive slices of widths (d_t, d_h, d_w) for (tau, h, w); inside a
+    slice of width d, pair j (channels 2j, 2j+1 of the slice) turns by
+        theta = coord * base_m ** (-2 j / d).
+    """
+    tags = np.asarray(tags)
+    pos = np.asarray(pos, np.float64)
+    n = tags.shape[0]
+    theta = np.zeros((n, D // 2), np.float64)
+    for m in (TEXT, VIDEO, AUDIO):
+        sel = tags == m
+        if not sel.any():
+            continue
+        cfg = rope[m]
+        tau = pos[sel, 0] * cfg.time_scale
+        if cfg.shift_time:
+            tau = tau + time_shift(time_offset)
+        coords = (tau, pos[sel, 1], pos[sel, 2])
+        widths = (cfg.d_t, cfg.d_h, cfg.d_w)
+        assert sum(widths) == D and all(w % 2 == 0 for w in widths)
+        pair0 = 0
+        for coord, d in zip(coords, widths):
+            if d == 0:
+                continue
+            j = np.arange(d // 2, dtype=np.float64)
+            inv_freq = cfg.base ** (-2.0 * j / d)
+            theta[np.nonzero(sel)[0][:, None], pair0 + np.arange(d // 2)[None, :]] = \
+                coord[:, None] * inv_freq[None, :]
+            pair0 += d // 2
+    return theta
+
+
+def apply_rope(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
+    """Rotate adjacent channel pairs of x [n, H, D] by theta [n, D/2]:
+    (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos), the same angle for every head."""
+    c = np.cos(theta)[:, None, :]
+    s = np.sin(theta)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x, dtype=np.float64)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def rope_qk(q, k, tags, pos, rope, time_offset):
+    """RoPE of Q and K in source order (V is not rotated)."""
+    theta = rope_angles(tags, pos, rope, time_offset, q.shape[-1])
+    return apply_rope(q, theta), apply_rope(k, theta)
+
+
+# ---------------------------------------------------------------------------
+# a3: attention inside each segment
+# ---------------------------------------------------------------------------
+def _scale(D: int, softmax_scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(D) if not softmax_scale else float(softmax_scale)
+
+
+def attention(q, k, v, cu, softmax_scale: Optional[float] = None, row_block: int = 1024):
+    """O[i,h] = sum_{j in seg(i)} softmax_j(Q[i,h].K[j,h] * scale) V[j,h].
+
+    q, k, v: float64 [rows, H, D] in packed order.  Rows at or past cu[-1] are
+    left at zero and nothing is read from them.  Query rows are processed
+    `row_block` at a time only to bound memory; every row is its own softmax.
+    """
+    rows, H, D = q.shape
+    sc = _scale(D, softmax_scale)
+    o = np.zeros((rows, H, D), np.float64)
+    for a, b in zip(np.asarray(cu[:-1], np.int64), np.asarray(cu[1:], np.int64)):
+        if b <= a:
+            continue
+        for h in range(H):
+            K = k[a:b, h, :]
+            V = v[a:b, h, :]
+            for r0 in range(a, b, row_block):
+                r1 = min(b, r0 + row_block)
+                S = (q[r0:r1, h, :] @ K.T) * sc
+                S = S - S.max(axis=1, keepdims=True)
+                P = np.exp(S)
+                P = P / P.sum(axis=1, keepdims=True)
+                o[r0:r1, h, :] = P @ V
+    return o
+
+
+def attention_rows(q, k, v, cu, rows: Sequence[int], heads: Optional[Sequence[int]] = None,
+                   softmax_scale: Optional[float] = None):
+    """The same definition evaluated only for the packed rows `rows` and heads
+    `heads`: returns float64 [len(rows), len(heads), D]."""
+    rows = np.asarray(rows, np.int64)
+    H, D = q.shape[1], q.shape[2]
+    heads = np.arange(H) if heads is None else np.asarray(heads, np.int64)
+    sc = _scale(D, softmax_scale)
+    cu = np.asarray(cu, np.int64)
+    out = np.zeros((rows.shape[0], heads.shape[0], D), np.float64)
+    seg_of = np.searchsorted(cu, rows, side="right") - 1
+    for s in np.unique(seg_of):
+        a, b = cu[s], cu[s + 1]
+        sel = np.nonzero(seg_of == s)[0]
+        for hi, h in enumerate(heads):
+            S = (q[rows[sel], h, :] @ k[a:b, h, :].T) * sc
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P = P / P.sum(axis=1, keepdims=True)
+            out[sel, hi, :] = P @ v[a:b, h, :]
+    return out
+
+
+def attention_weights(q, k, cu, softmax_scale: Optional[float] = None):
+    """Full [H, rows, rows] softmax weight matrix of the packed sequence, zero
+    outside the segment blocks (small inputs only)."""
+    rows, H, D = q.shape
+    sc = _scale(D, softmax_scale)
+    P = np.zeros((H, rows, rows), np.float64)
+    for a, b in zip(np.asarray(cu[:-1], np.int64), np.asarray(cu[1:], np.int64)):
+        if b <= a:
+            continue
+        for h in range(H):
+            S = (q[a:b, h, :] @ k[a:b, h, :].T) * sc
+            S = S - S.max(axis=1, keepdims=True)
+            E = np.exp(S)
+            P[h, a:b, a:b] = E / E.sum(axis=1, keepdims=True)
+    return P
+
+
+# ---------------------------------------------------------------------------
+# a4: unpack by modality
+# ---------------------------------------------------------------------------
+def unpack(o, perm, tags):
+    """For each modality m (text, video, audio): idx_m lists the packed row of
+    every source token with tag m, in source order, and out_m = o[idx_m]."""
+    perm = np.asarray(perm, np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.shape[0])
+    tags = np.asarray(tags)
+    outs, idxs = [], []
+    for m in (TEXT, VIDEO, AUDIO):
+        src = np.nonzero(tags == m)[0]
+        idx = inv[src]
+        idxs.append(idx.astype(np.int32))
+        outs.append(o[idx])
+    return outs, idxs
+
+
+# ---------------------------------------------------------------------------
+# the whole path
+# ---------------------------------------------------------------------------
+def run(q_src, k_src, v_src, tags, pos, seg, n_seg, rope, time_offset,
+        softmax_scale: Optional[float] = None):
+    """Pack -> RoPE -> attention -> unpack on float64 source-order inputs.
+
+    Returns a dict with cu, perm, packed q/k/v (after RoPE), o (packed order),
+    outs (per modality) and idxs (per modality)."""
+    cu, perm = pack(seg, n_seg)
+    qr, kr = rope_qk(q_src, k_src, tags, pos, rope, time_offset)
+    qp, kp, vp = qr[perm], kr[perm], v_src[perm]
+    o = attention(qp, kp, vp, cu, softmax_scale)
+    outs, idxs = unpack(o, perm, tags)
+    return dict(cu=cu, perm=perm, q=qp, k=kp, v=vp, o=o, outs=outs, idxs=idxs)

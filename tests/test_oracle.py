@@ -1,0 +1,362 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every check is a printed page
+value, a closed form, an identity of rotations / softmax, an independent
+formulation (complex numbers, torch's float64 SDPA) or brute force in pure
+Python on tiny inputs.
+"""
+import cmath
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = []
+
+
+def _f64(wl, seed=None):
+    q, k, v = W.make_qkv(wl, seed=seed)
+    return W.to_f64(q), W.to_f64(k), W.to_f64(v)
+
+
+# ---------------------------------------------------------------- page values
+def test_page_cu_seqlens_examples(golden):
+    ex2 = golden["cu_seqlens_text_video"]
+    wl = W.make_custom([10, 20], H=1, D=64, modalities=[W.TEXT, W.VIDEO])
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    assert cu.tolist() == ex2["cu_seqlens"]
+    ex3 = golden["cu_seqlens_text_video_audio"]
+    wl0 = W.make_workload(0)
+    cu, perm = oracle.pack(wl0.seg, wl0.n_seg)
+    assert cu.tolist() == ex3["cu_seqlens"]
+    assert perm.tolist() == list(range(45))
+    assert [(g[0], g[2]) for g in wl0.groups] == [tuple(x) for x in ex3["groups"]]
+
+
+def test_page_exact_zero_weights(golden):
+    """Token 15 (video) dots only with keys 10..29; keys 0..9 get weight exactly 0."""
+    ex = golden["cu_seqlens_text_video"]
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    qr, kr = oracle.rope_qk(q, k, wl.tags, wl.pos, wl.rope, wl.time_offset)
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    P = oracle.attention_weights(qr[perm], kr[perm], cu)
+    lo, hi = ex["visible_keys"]
+    z0, z1 = ex["zero_weight_keys"]
+    i = ex["query"]
+    for h in range(wl.H):
+        assert np.all(P[h, i, z0:z1 + 1] == 0.0)
+        assert np.all(P[h, i, hi + 1:] == 0.0)
+        assert np.all(P[h, i, lo:hi + 1] > 0.0)
+        assert abs(P[h, i, lo:hi + 1].sum() - 1.0) < 1e-15
+    # every off-diagonal block is exactly zero; every row sums to one
+    mask = np.zeros((wl.n, wl.n), bool)
+    for a, b in zip(cu[:-1], cu[1:]):
+        mask[a:b, a:b] = True
+    assert np.all(P[:, ~mask] == 0.0)
+    assert np.allclose(P.sum(axis=2), 1.0, atol=1e-15, rtol=0)
+
+
+def test_page_trim_numbers(golden):
+    ex = golden["trim_padding"]
+    assert ex["aligned_length"] - ex["effective_tokens"] == ex["padding"]
+    assert ex["aligned_length"] == 919 * W.ALIGN
+    wl2 = W.make_workload(2)
+    assert wl2.n == ex["effective_tokens"] and wl2.capacity == ex["aligned_length"]
+    # aligned already: trimming is a no-op
+    wl4 = W.make_workload(4)
+    assert wl4.capacity == wl4.n
+
+
+def test_page_time_shift(golden):
+    ex = golden["time_shift"]
+    s = ex["window_start_frame"]
+    d = oracle.time_shift(s)
+    assert abs(d - 1190.0 / 3.0) < 1e-12            # 238 * 40 / 24 = 396.666...
+    assert round(d, ex["printed_decimals"]) == ex["shift_printed"]
+    assert d != int(d)                              # the fraction is kept
+
+
+def test_page_continuation_order(golden):
+    ex = golden["continuation_order"]
+    wl = W.make_workload(3)
+    mods = [g[1] for g in wl.groups]
+    assert mods == [W.TEXT, W.AUDIO, W.VIDEO, W.AUDIO, W.VIDEO]
+    assert len(ex["order"]) == len(wl.groups) == 5
+    assert wl.groups[2][2] == ex["video_reference_frames"] * 48 * 84
+    assert wl.n_seg == 1 and wl.time_offset == golden["time_shift"]["window_start_frame"]
+
+
+def test_window_partition_closed_forms():
+    """Regular 4x8x8 windows over 16x64x112: 4*8*14 = 448 windows of 256.
+    Half-shifted: 5*9*15 = 675 edge-cropped windows; sizes 256/128/64/32 occur
+    3*7*13 / (2*7*13 + 3*2*13 + 3*7*2) / (2*2*13 + 2*7*2 + 3*2*2) / 2*2*2 times."""
+    reg = W.make_workload(4, shifted=False)
+    L = reg.segment_lengths()
+    assert reg.n_seg == 448 and np.all(L == 256)
+    sh = W.make_workload(4)
+    L = sh.segment_lengths()
+    assert sh.n_seg == 675 and L.sum() == 114688
+    sizes, counts = np.unique(L, return_counts=True)
+    expect = {256: 3 * 7 * 13, 128: 2 * 7 * 13 + 3 * 2 * 13 + 3 * 7 * 2,
+              64: 2 * 2 * 13 + 2 * 7 * 2 + 3 * 2 * 2, 32: 2 * 2 * 2}
+    assert dict(zip(sizes.tolist(), counts.tolist())) == expect
+
+
+# ---------------------------------------------------------------------- pack
+def _pack_brute(seg, n_seg):
+    perm, cu = [], [0]
+    for s in range(n_seg):
+        members = [i for i in range(len(seg)) if seg[i] == s]
+        perm += members
+        cu.append(cu[-1] + len(members))
+    return cu, perm
+
+
+@pytest.mark.parametrize("case", ["c4_shifted", "random", "empty_segments"])
+def test_pack_stable_bruteforce(case):
+    rng = np.random.default_rng(7)
+    if case == "c4_shifted":
+        wl = W.make_workload(4)
+        seg, n_seg = wl.seg[:6000], wl.n_seg      # a prefix: still unsorted windows
+    elif case == "random":
+        seg, n_seg = rng.integers(0, 13, size=500).astype(np.int32), 13
+    else:
+        seg, n_seg = np.array([3, 3, 0, 5, 0, 3], np.int32), 7
+    cu, perm = oracle.pack(seg, n_seg)
+    cu_b, perm_b = _pack_brute(seg.tolist(), n_seg)
+    assert cu.tolist() == cu_b and perm.tolist() == perm_b
+    assert cu.dtype == np.int32 and perm.dtype == np.int32
+
+
+# ---------------------------------------------------------------------- RoPE
+def test_rope_frequencies_textbook_values():
+    """RoFormer: pair j of a d-wide slice turns by pos * 10000^(-2j/d).
+    Values below are written out, not recomputed with the oracle's formula."""
+    wl = W.make_custom([4], H=1, D=64, modalities=[W.TEXT])
+    th = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 0.0, 64)
+    assert np.all(th[0] == 0.0)                              # position 0: no rotation
+    assert th[1, 0] == 1.0                                   # pair 0 turns 1 rad per unit
+    assert abs(th[1, 1] - 0.7498942093324559) < 1e-15        # 10000^(-1/32)
+    assert abs(th[1, 16] - 0.01) < 1e-15                     # 10000^(-1/2)
+    assert abs(th[3, 31] - 3 * 1.333521432163324e-4) < 1e-18  # 3 * 10000^(-31/32)
+
+
+def test_rope_complex_form_bruteforce():
+    """The rotation equals (x0 + i x1) * exp(i theta) (pure-Python complex)."""
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    th = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 0.0, wl.D)
+    qr = oracle.apply_rope(q, th)
+    for i in range(0, wl.n, 7):
+        for h in range(wl.H):
+            for j in range(wl.D // 2):
+                z = complex(q[i, h, 2 * j], q[i, h, 2 * j + 1]) * cmath.exp(1j * th[i, j])
+                assert abs(z.real - qr[i, h, 2 * j]) < 1e-14
+                assert abs(z.imag - qr[i, h, 2 * j + 1]) < 1e-14
+
+
+def test_rope_norm_and_relative_position():
+    """|pair| is kept; <R(p) q, R(p') k> = <q, R(p'-p) k> for one 1-D scheme."""
+    rng = np.random.default_rng(3)
+    D = 64
+    wl = W.make_custom([50], H=1, D=D, modalities=[W.TEXT])
+    th = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 0.0, D)
+    x = rng.standard_normal((50, 1, D))
+    xr = oracle.apply_rope(x, th)
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = xr[..., 0::2] ** 2 + xr[..., 1::2] ** 2
+    assert np.allclose(n0, n1, rtol=1e-13, atol=0)
+    q = np.repeat(rng.standard_normal((1, 1, D)), 50, axis=0)
+    k = np.repeat(rng.standard_normal((1, 1, D)), 50, axis=0)
+    qr, kr = oracle.apply_rope(q, th), oracle.apply_rope(k, th)
+    for p, pp in [(3, 10), (20, 27), (0, 7), (40, 47), (12, 5), (30, 23)]:
+        lhs = float(qr[p, 0] @ kr[pp, 0])
+        if pp >= p:       # R(pp - p) k is k rotated to text position pp - p
+            rhs = float(q[0, 0] @ kr[pp - p, 0])
+        else:             # negative offset: rotate k backwards by position p - pp
+            back = oracle.apply_rope(k[:1], -th[p - pp:p - pp + 1])
+            rhs = float(q[0, 0] @ back[0, 0])
+        assert abs(lhs - rhs) < 1e-12
+    # same offset, different absolute positions: same score
+    assert abs(float(qr[3, 0] @ kr[10, 0]) - float(qr[20, 0] @ kr[27, 0])) < 1e-12
+
+
+def test_rope_video_slices_and_audio_scale():
+    D = 64
+    wl = W.make_workload(0)          # video grid t 0..4, h 0..1, w 0..1; audio ticks 0..14
+    th = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 0.0, D)
+    vid = np.nonzero(wl.tags == W.VIDEO)[0]
+    d_t, d_h, d_w = 16, 24, 24
+    for i in vid:
+        t, h, w = wl.pos[i]
+        assert th[i, 0] == t and th[i, d_t // 2] == h and th[i, (d_t + d_h) // 2] == w
+        if h == 0 and w == 0:
+            assert np.all(th[i, d_t // 2:] == 0.0)
+        # t slice is 1-D RoPE of width 16: pair j turns t * 10000^(-2j/16)
+        assert abs(th[i, 1] - t * 10000 ** (-1 / 8)) < 1e-14
+        assert abs(th[i, d_t // 2 + 1] - h * 10000 ** (-1 / 12)) < 1e-14
+    # audio tick 5 at 40 Hz is 3.0 video frames: same angles as text index 3
+    aud = np.nonzero(wl.tags == W.AUDIO)[0]
+    txt = np.nonzero(wl.tags == W.TEXT)[0]
+    assert np.allclose(th[aud[5]], th[txt[3]], rtol=1e-15, atol=0)
+
+
+def test_rope_time_shift_applies_to_time_axis_only():
+    D = 64
+    wl = W.make_workload(0)
+    th0 = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 0.0, D)
+    th1 = oracle.rope_angles(wl.tags, wl.pos, wl.rope, 238.0, D)
+    delta = 1190.0 / 3.0
+    txt = wl.tags == W.TEXT
+    vid = wl.tags == W.VIDEO
+    aud = wl.tags == W.AUDIO
+    assert np.array_equal(th0[txt], th1[txt])                       # text: no shift
+    assert np.allclose(th1[vid, 0] - th0[vid, 0], delta, rtol=0, atol=1e-12)
+    assert np.array_equal(th0[vid, 8:], th1[vid, 8:])               # h, w untouched
+    assert np.allclose(th1[aud, 0] - th0[aud, 0], delta, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- attention
+def _sdpa_per_segment(q, k, v, cu):
+    out = np.zeros_like(q)
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b <= a:
+            continue
+        Q = torch.from_numpy(q[a:b]).permute(1, 0, 2).unsqueeze(0)
+        K = torch.from_numpy(k[a:b]).permute(1, 0, 2).unsqueeze(0)
+        V = torch.from_numpy(v[a:b]).permute(1, 0, 2).unsqueeze(0)
+        O = torch.nn.functional.scaled_dot_product_attention(Q, K, V)
+        out[a:b] = O[0].permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("lengths", [[10, 20, 15], [1, 0, 33, 64, 65, 3], [200]])
+def test_attention_vs_torch_sdpa(lengths):
+    wl = W.make_custom(lengths, H=3, D=64, dtype="f32", q_scale=1.0)
+    q, k, v = _f64(wl)
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    o = oracle.attention(q[perm], k[perm], v[perm], cu)
+    ref = _sdpa_per_segment(q[perm], k[perm], v[perm], cu)
+    assert np.max(np.abs(o - ref)) < 1e-13
+    rows = np.arange(0, wl.n, 5)
+    o_rows = oracle.attention_rows(q[perm], k[perm], v[perm], cu, rows, heads=[2, 0])
+    assert np.max(np.abs(o_rows - ref[rows][:, [2, 0]])) < 1e-13
+
+
+def test_attention_bruteforce_tiny():
+    """Pure-Python triple loop with math.exp on the 45-token workload."""
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    o = oracle.attention(q, k, v, cu)
+    D = wl.D
+    for (a, b) in zip(cu[:-1].tolist(), cu[1:].tolist()):
+        for h in range(wl.H):
+            for i in range(a, b):
+                s = [sum(q[i, h, d] * k[j, h, d] for d in range(D)) / math.sqrt(D) for j in range(a, b)]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                z = sum(e)
+                for d in range(0, D, 9):
+                    ref = sum(e[j - a] * v[j, h, d] for j in range(a, b)) / z
+                    assert abs(ref - o[i, h, d]) < 1e-13
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(11)
+    H, D = 2, 64
+    cu = np.array([0, 1, 9, 40], np.int32)          # a length-1 segment, then two more
+    q = rng.standard_normal((40, H, D))
+    k = rng.standard_normal((40, H, D))
+    v = rng.standard_normal((40, H, D))
+    o = oracle.attention(q, k, v, cu)
+    assert np.array_equal(o[0], v[0])                                   # L = 1 -> V
+    o = oracle.attention(np.zeros_like(q), k, v, cu)                     # Q = 0 -> mean V
+    assert np.allclose(o[1:9], v[1:9].mean(axis=0, keepdims=True), atol=1e-14, rtol=0)
+    assert np.allclose(o[9:40], v[9:40].mean(axis=0, keepdims=True), atol=1e-14, rtol=0)
+    vc = np.full_like(v, 0.375)                                          # constant V
+    assert np.allclose(oracle.attention(q, k, vc, cu), 0.375, atol=1e-15, rtol=0)
+    ks = np.repeat(k[9:10], 40, axis=0)                                  # identical keys
+    o = oracle.attention(q, ks, v, cu)
+    assert np.allclose(o[9:40], v[9:40].mean(axis=0, keepdims=True), atol=1e-14, rtol=0)
+
+
+def test_attention_packed_equals_segments_alone_and_pad_rows_unread():
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    cap = wl.capacity
+    pad = lambda x: np.concatenate([x, np.full((cap - wl.n,) + x.shape[1:], np.nan)])
+    o = oracle.attention(pad(q), pad(k), pad(v), cu)
+    assert np.all(o[wl.n:] == 0.0) and np.all(np.isfinite(o))
+    for a, b in zip(cu[:-1], cu[1:]):
+        alone = oracle.attention(q[a:b], k[a:b], v[a:b], np.array([0, b - a]))
+        assert np.array_equal(alone, o[a:b])
+
+
+def test_attention_key_permutation_invariance():
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    o = oracle.attention(q, k, v, cu)
+    rng = np.random.default_rng(5)
+    p = np.arange(wl.n)
+    for a, b in zip(cu[:-1], cu[1:]):
+        p[a:b] = a + rng.permutation(b - a)
+    o2 = oracle.attention(q, k[p], v[p], cu)
+    assert np.max(np.abs(o - o2)) < 1e-13
+
+
+@pytest.mark.parametrize("which", ["tiny", "windows"])
+def test_time_shift_invariance_end_to_end(which):
+    """Shifting every time coordinate of a single-modality segment by a
+    constant leaves attention unchanged (RoPE depends on differences only)."""
+    if which == "tiny":
+        wl = W.make_workload(0)
+    else:
+        wl = W.make_custom([40, 24, 37], H=2, D=64, dtype="f32", q_scale=1.0)
+    q, k, v = _f64(wl)
+    r0 = oracle.run(q, k, v, wl.tags, wl.pos, wl.seg, wl.n_seg, wl.rope, 0.0)
+    r1 = oracle.run(q, k, v, wl.tags, wl.pos, wl.seg, wl.n_seg, wl.rope, 238.0)
+    pos2 = wl.pos.copy()
+    pos2[:, 0] += 17
+    r2 = oracle.run(q, k, v, wl.tags, pos2, wl.seg, wl.n_seg, wl.rope, 0.0)
+    for r in (r1, r2):
+        assert np.max(np.abs(r["o"] - r0["o"])) < 1e-12
+        assert np.max(np.abs(r["q"] - r0["q"])) > 1e-3      # RoPE itself did change
+
+
+# -------------------------------------------------------------------- unpack
+def test_unpack_bruteforce_and_grid_order():
+    wl = W.make_workload(4)
+    n = 3000
+    seg = wl.seg[:n]
+    cu, perm = oracle.pack(seg, wl.n_seg)
+    o = np.arange(n, dtype=np.float64)[:, None, None] * np.ones((1, 1, 2))
+    o = o[perm]                                   # packed copy of a source-indexed ramp
+    tags = wl.tags[:n].copy()
+    tags[::7] = W.TEXT
+    tags[3::11] = W.AUDIO
+    outs, idxs = oracle.unpack(o, perm, tags)
+    perm_l = perm.tolist()
+    for m in (W.TEXT, W.VIDEO, W.AUDIO):
+        expect_idx = [perm_l.index(i) for i in range(n) if tags[i] == m]
+        assert idxs[m].tolist() == expect_idx
+        # source order restored: the ramp reads back as the source indices of modality m
+        assert outs[m][:, 0, 0].tolist() == [float(i) for i in range(n) if tags[i] == m]
+    assert sorted(np.concatenate(idxs).tolist()) == list(range(n))
+
+
+def test_run_end_to_end_tiny():
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    r = oracle.run(q, k, v, wl.tags, wl.pos, wl.seg, wl.n_seg, wl.rope, wl.time_offset)
+    assert r["cu"].tolist() == [0, 10, 30, 45]
+    assert [x.shape[0] for x in r["outs"]] == [10, 20, 15]
+    ref = _sdpa_per_segment(r["q"], r["k"], r["v"], r["cu"])
+    assert np.max(np.abs(r["o"] - ref)) < 1e-13
