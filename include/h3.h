@@ -1,0 +1,168 @@
+/*
+ * h3.h — C ABI of the packed varlen modality-RoPE attention library (libh3.so).
+ *
+ * The path: text, video-latent and audio-latent token rows are packed into one
+ * 1-D sequence split into mutually invisible sub-sequences by cu_seqlens; RoPE
+ * with modality-selected frequencies is applied to Q and K; attention runs
+ * inside each sub-sequence; the output is sliced back per modality.
+ *
+ * Pages cited below:
+ *   [P1] "生产环境下的音视频联合生成：MiniMax-H3 与 vLLM-Omni 架构解析"
+ *   [P3] "突破视频生成大模型的工程瓶颈"
+ *
+ * Conventions shared by every call:
+ *   - Device buffers are owned and allocated by the caller.  The library never
+ *     allocates, keeps no state between calls and is re-entrant.  Calls that
+ *     need scratch memory take a caller workspace whose size the matching
+ *     h3_*_workspace_bytes() function returns; its contents need not be
+ *     initialised and are meaningless after the call.
+ *   - Tensors are contiguous, token-major [rows][H][D], 16-byte aligned.
+ *     Element type is given by h3_dtype (bf16 = IEEE bfloat16, f32 = float).
+ *   - Work is enqueued on `stream` and the call returns without waiting,
+ *     except h3_validate_seqlens, which synchronises.
+ *   - Errors that the host can see (NULL pointers, sizes, dtype, alignment,
+ *     workspace size) return a non-zero h3_status before anything is
+ *     launched.  A failed launch returns H3_ERR_HIP.  Device-side data
+ *     (cu_seqlens, segment ids, tags) is checked by h3_validate_seqlens, not
+ *     by the hot calls; malformed device data gives unspecified values but no
+ *     access outside the buffers described here.
+ */
+#ifndef H3_H
+#define H3_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  H3_OK = 0,
+  H3_ERR_NULL = 1,         /* a required pointer is NULL */
+  H3_ERR_DTYPE = 2,        /* unknown h3_dtype */
+  H3_ERR_SHAPE = 3,        /* negative or inconsistent n / n_seg / H / D / rows */
+  H3_ERR_SEQLENS = 4,      /* cu_seqlens not monotone, cu[0] != 0 (validate only) */
+  H3_ERR_CAPACITY = 5,     /* rows do not fit the output capacity */
+  H3_ERR_UNSUPPORTED = 6,  /* D not in {64, 128}, RoPE split invalid, bad scale */
+  H3_ERR_HIP = 7,          /* a HIP launch or runtime call failed */
+  H3_ERR_WORKSPACE = 8,    /* workspace NULL or smaller than required */
+  H3_ERR_ALIGN = 9         /* a tensor pointer is not 16-byte aligned */
+} h3_status;
+
+/* Modality tags, one uint8 per token ([P1] section 三: discrete text / video /
+ * audio label on every token, selecting the RoPE frequencies). */
+typedef enum { H3_TEXT = 0, H3_VIDEO = 1, H3_AUDIO = 2 } h3_modality;
+
+typedef enum { H3_BF16 = 0, H3_F32 = 1 } h3_dtype;
+
+/* RoPE of one modality.  A token with position (t, h, w) has time coordinate
+ *   tau = t * time_scale + (shift_time ? s * 40 / 24 : 0)
+ * ([P3] long-video continuation, step 3: t_global = t_local + s * 40 / 24,
+ * 40 Hz audio latents over 24 FPS video, fraction kept; time axis only).
+ * The head dim is cut into consecutive slices of widths d_t, d_h, d_w
+ * (d_t + d_h + d_w = D, each even) for tau, h and w.  Inside a slice of width
+ * d, channels (2j, 2j+1) are rotated by theta = coord * base^(-2j/d):
+ *   (x0, x1) -> (x0 cos theta - x1 sin theta, x0 sin theta + x1 cos theta). */
+typedef struct {
+  double base;
+  double time_scale;
+  int32_t shift_time;
+  int32_t d_t, d_h, d_w;
+} h3_rope_modality;
+
+typedef struct { h3_rope_modality m[3]; } h3_rope_cfg;   /* indexed by h3_modality */
+
+/* ------------------------------------------------------------------------ */
+/* Pack + modality RoPE ([P1] section 三: source rows -> packed 1-D sequence
+ * with cu_seqlens; modality tags select RoPE; [P3] continuation time shift).
+ *
+ *   q_src, k_src, v_src : [n][H][D] in source order (device, read only)
+ *   tags                : uint8 [n], h3_modality per token (device).  A tag
+ *                         outside 0..2 leaves that row unrotated.
+ *   pos_thw             : int32 [n][3], (t, h, w) per token (device)
+ *   seg_id              : int32 [n], sub-sequence of each token, 0..n_seg-1
+ *                         (device).  A token with an id outside that range is
+ *                         dropped (then cu_seqlens[n_seg] < n).
+ *   rope                : host struct; time_offset_frames = s of the shift.
+ *   q_out, k_out        : [capacity][H][D] packed, Q and K rotated (device)
+ *   v_out               : [capacity][H][D] packed V, or NULL to skip V
+ *   cu_seqlens          : int32 [n_seg+1] out: cu[0] = 0, segment k occupies
+ *                         packed rows [cu[k], cu[k+1])
+ *   perm                : int32 [n] out: perm[p] = source row at packed row p
+ * Packed order is the stable order by segment id: rows of one segment keep
+ * their source order.  Rows [cu[n_seg], capacity) are not written.
+ * Requires n <= capacity; n = 0 is a no-op apart from cu_seqlens = 0.
+ * Rotation: fp64 angle and cos/sin, fp32 rotation, one RNE rounding on store. */
+size_t h3_pack_workspace_bytes(int32_t n, int32_t n_seg);
+h3_status h3_pack_rope(const void* q_src, const void* k_src, const void* v_src,
+                       const uint8_t* tags, const int32_t* pos_thw, const int32_t* seg_id,
+                       int32_t n, int32_t n_seg, int32_t H, int32_t D, h3_dtype dt,
+                       const h3_rope_cfg* rope, double time_offset_frames,
+                       void* q_out, void* k_out, void* v_out, int32_t capacity,
+                       int32_t* cu_seqlens, int32_t* perm,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Varlen attention forward ([P1] section 三: a token attends only to keys of
+ * its own sub-sequence, softmax normalised inside it, weight zero outside;
+ * bidirectional.  [P1] section 六: rows past the effective length are
+ * trimmed by a length, not a copy).
+ *
+ *   q, k, v      : packed [>= total_rows][H][D] (device)
+ *   cu_seqlens   : int32 [n_seg+1] (device), non-decreasing, cu[0] = 0
+ *   max_seqlen   : host hint, >= every segment length (selects tile shapes;
+ *                  results do not depend on it)
+ *   total_rows   : host, = cu_seqlens[n_seg]; rows >= total_rows are neither
+ *                  read nor written, whatever they hold (pad rows may be NaN)
+ *   softmax_scale: 0 -> 1/sqrt(D)
+ *   o            : packed [>= total_rows][H][D] out, rows < total_rows written
+ * O[i,h] = sum_{j in seg(i)} softmax_j(scale * Q[i,h].K[j,h]) V[j,h].
+ * bf16: bf16 MFMA with fp32 accumulation and fp32 online softmax, P rounded
+ * to bf16 for the PV product, one RNE rounding of O.  f32: fp32 throughout.
+ * Supported D: 64 and 128.  Tiles never cross a cu_seqlens boundary, so no
+ * FLOP is spent on masked pairs and each segment's output is bit-identical
+ * to that segment computed alone. */
+size_t h3_attn_workspace_bytes(int32_t total_rows, int32_t n_seg);
+h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
+                             int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                             float softmax_scale, void* o,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Unpack by modality ([P1] section 三: the output sequence is sliced by
+ * modality into per-modality velocities; [P3] window-aligned SP: token order
+ * restored after attention).
+ *
+ *   o          : packed [>= n][H][D] (device)
+ *   perm       : int32 [n] from h3_pack_rope (device)
+ *   tags_src   : uint8 [n] in source order (device)
+ *   out[m]     : [n_per_mod[m]][H][D] out, or NULL to skip the copy
+ *   idx[m]     : int32 [n_per_mod[m]] out (packed row of each token), or NULL
+ *   n_per_mod  : host int32[3], number of tokens with tag m
+ * For modality m, token k (k-th token of tag m in source order) gets
+ * idx[m][k] = packed row p with perm[p] = its source row, and out[m][k] = o[p].
+ * Exact copy: no arithmetic on values. */
+size_t h3_unpack_workspace_bytes(int32_t n);
+h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_t* tags_src,
+                                int32_t n, int32_t H, int32_t D, h3_dtype dt,
+                                void* const out[3], int32_t* const idx[3],
+                                const int32_t n_per_mod[3],
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Checks cu_seqlens on the device: cu[0] == 0, non-decreasing,
+ * cu[n_seg] <= capacity.  Synchronises `stream`.  Returns H3_OK,
+ * H3_ERR_SEQLENS or H3_ERR_CAPACITY. */
+h3_status h3_validate_seqlens(const int32_t* cu_seqlens, int32_t n_seg, int32_t capacity,
+                              hipStream_t stream);
+
+const char* h3_status_string(h3_status s);
+const char* h3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3_H */

@@ -1,0 +1,20 @@
+"""Packed varlen modality-RoPE attention for AMD MI355X (gfx950).
+
+The three calls of the path, each a thin wrapper over the C ABI of libh3.so
+(include/h3.h) whose work runs in hand-written HIP kernels:
+
+  pack_rope(q, k, v, tags, pos, seg, n_seg, rope, s)  -> packed Q', K', V, cu_seqlens, perm
+  varlen_attn_fwd(q, k, v, cu_seqlens, total_rows)   -> O
+  unpack_by_modality(o, perm, tags, n_per_mod)       -> per-modality outputs and row indices
+
+Build the library in-tree first: ``python -m packed_varlen_attention_amd.build``.
+"""
+from ._lib import (H3Error, H3_BF16, H3_F32, TEXT, VIDEO, AUDIO, LIB_PATH, SIGNATURES, load,
+                   status_string, version, pack_rope, varlen_attn_fwd, unpack_by_modality,
+                   validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
+                   unpack_workspace_bytes, workspace, rope_cfg)
+
+__all__ = ["H3Error", "H3_BF16", "H3_F32", "TEXT", "VIDEO", "AUDIO", "LIB_PATH", "SIGNATURES",
+           "load", "status_string", "version", "pack_rope", "varlen_attn_fwd",
+           "unpack_by_modality", "validate_seqlens", "pack_workspace_bytes",
+           "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg"]

@@ -1,0 +1,246 @@
+"""ctypes binding over libh3.so (include/h3.h).
+
+Argument marshalling only: shapes and dtypes of torch tensors are checked,
+pointers and the current HIP stream are passed to the C ABI, and a non-zero
+status raises H3Error.  Every step of the path runs in the library's HIP
+kernels; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libh3.so")
+
+H3_BF16, H3_F32 = 0, 1
+TEXT, VIDEO, AUDIO = 0, 1, 2
+
+# Every function include/h3.h declares, with (restype, argtypes).
+_c = ctypes
+_vp, _i32, _f32, _f64, _sz = _c.c_void_p, _c.c_int32, _c.c_float, _c.c_double, _c.c_size_t
+
+
+class h3_rope_modality(_c.Structure):
+    _fields_ = [("base", _f64), ("time_scale", _f64), ("shift_time", _i32),
+                ("d_t", _i32), ("d_h", _i32), ("d_w", _i32)]
+
+
+class h3_rope_cfg(_c.Structure):
+    _fields_ = [("m", h3_rope_modality * 3)]
+
+
+SIGNATURES = {
+    "h3_pack_workspace_bytes": (_sz, [_i32, _i32]),
+    "h3_pack_rope": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _c.c_int,
+                                _c.POINTER(h3_rope_cfg), _f64, _vp, _vp, _vp, _i32, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "h3_attn_workspace_bytes": (_sz, [_i32, _i32]),
+    "h3_varlen_attn_fwd": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _c.c_int,
+                                      _f32, _vp, _vp, _sz, _vp]),
+    "h3_unpack_workspace_bytes": (_sz, [_i32]),
+    "h3_unpack_by_modality": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _c.c_int,
+                                         _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_i32),
+                                         _vp, _sz, _vp]),
+    "h3_validate_seqlens": (_c.c_int, [_vp, _i32, _i32, _vp]),
+    "h3_status_string": (_c.c_char_p, [_c.c_int]),
+    "h3_version": (_c.c_char_p, []),
+}
+
+_LIB = None
+
+
+class H3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libh3.so; fails loudly if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libh3.so is not built (%s); run `python -m packed_varlen_attention_amd.build`"
+                              % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return load().h3_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load().h3_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise H3Error(status, where)
+
+
+# --------------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return H3_BF16
+    if t.dtype == torch.float32:
+        return H3_F32
+    raise TypeError("tensor dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def rope_cfg(rope: Sequence) -> h3_rope_cfg:
+    """Build the C struct from three objects with base, time_scale,
+    shift_time, d_t, d_h, d_w attributes (text, video, audio)."""
+    cfg = h3_rope_cfg()
+    for m in range(3):
+        r = rope[m]
+        cfg.m[m] = h3_rope_modality(float(r.base), float(r.time_scale), int(r.shift_time),
+                                    int(r.d_t), int(r.d_h), int(r.d_w))
+    return cfg
+
+
+def workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ the calls
+def pack_workspace_bytes(n: int, n_seg: int) -> int:
+    return int(load().h3_pack_workspace_bytes(n, n_seg))
+
+
+def attn_workspace_bytes(total_rows: int, n_seg: int) -> int:
+    return int(load().h3_attn_workspace_bytes(total_rows, n_seg))
+
+
+def unpack_workspace_bytes(n: int) -> int:
+    return int(load().h3_unpack_workspace_bytes(n))
+
+
+def pack_rope(q_src, k_src, v_src, tags, pos, seg, n_seg: int, rope, time_offset: float = 0.0,
+              capacity: Optional[int] = None, *, q_out=None, k_out=None, v_out=None, cu=None,
+              perm=None, ws=None, pack_v: bool = True, stream=None):
+    """h3_pack_rope.  Returns (q_out, k_out, v_out or None, cu_seqlens, perm)."""
+    torch = _torch()
+    lib = load()
+    n, H, D = q_src.shape
+    dev = q_src.device
+    cap = n if capacity is None else int(capacity)
+    if tags.dtype != torch.uint8 or pos.dtype != torch.int32 or seg.dtype != torch.int32:
+        raise TypeError("tags must be uint8, pos and seg int32")
+    if tuple(pos.shape) != (n, 3) or tags.shape[0] != n or seg.shape[0] != n:
+        raise ValueError("tags [n], pos [n,3] and seg [n] must match q_src rows")
+    if k_src.shape != q_src.shape or (v_src is not None and v_src.shape != q_src.shape):
+        raise ValueError("q_src, k_src, v_src shapes differ")
+    if q_out is None:
+        q_out = torch.empty((cap, H, D), dtype=q_src.dtype, device=dev)
+    if k_out is None:
+        k_out = torch.empty((cap, H, D), dtype=q_src.dtype, device=dev)
+    if pack_v and v_out is None:
+        v_out = torch.empty((cap, H, D), dtype=q_src.dtype, device=dev)
+    if not pack_v:
+        v_out = None
+    for t in (q_out, k_out) + ((v_out,) if v_out is not None else ()):
+        if t.shape[0] < cap or tuple(t.shape[1:]) != (H, D) or t.dtype != q_src.dtype:
+            raise ValueError("output buffers must be [capacity, H, D] of the input dtype")
+    if cu is None:
+        cu = torch.empty(n_seg + 1, dtype=torch.int32, device=dev)
+    if perm is None:
+        perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(lib.h3_pack_workspace_bytes(n, n_seg), dev)
+    cfg = rope_cfg(rope)
+    st = lib.h3_pack_rope(_ptr(q_src), _ptr(k_src), _ptr(v_src) if v_out is not None else None,
+                          _ptr(tags), _ptr(pos), _ptr(seg), n, int(n_seg), H, D, _dt(q_src),
+                          ctypes.byref(cfg), float(time_offset), _ptr(q_out), _ptr(k_out),
+                          _ptr(v_out), cap, _ptr(cu), _ptr(perm), _ptr(ws), ws.numel(),
+                          _stream(stream))
+    _check(st, "h3_pack_rope")
+    return q_out, k_out, v_out, cu, perm
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens, total_rows: int, max_seqlen: int = 0,
+                    softmax_scale: float = 0.0, *, o=None, ws=None, stream=None):
+    """h3_varlen_attn_fwd on packed [rows, H, D] tensors.  Returns o."""
+    torch = _torch()
+    lib = load()
+    rows, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if total_rows > rows:
+        raise ValueError("total_rows exceeds the tensors' rows")
+    n_seg = cu_seqlens.shape[0] - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(lib.h3_attn_workspace_bytes(total_rows, n_seg), q.device)
+    st = lib.h3_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), n_seg, int(max_seqlen),
+                                int(total_rows), H, D, _dt(q), float(softmax_scale), _ptr(o),
+                                _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "h3_varlen_attn_fwd")
+    return o
+
+
+def unpack_by_modality(o, perm, tags_src, n_per_mod: Sequence[int], *, outs=None, idxs=None,
+                       ws=None, copy_values: bool = True, stream=None):
+    """h3_unpack_by_modality.  Returns (outs[3], idxs[3])."""
+    torch = _torch()
+    lib = load()
+    n = tags_src.shape[0]
+    _, H, D = o.shape
+    dev = o.device
+    if tags_src.dtype != torch.uint8 or perm.dtype != torch.int32:
+        raise TypeError("tags_src must be uint8 and perm int32")
+    if outs is None:
+        outs = [torch.empty((int(c), H, D), dtype=o.dtype, device=dev) if copy_values else None
+                for c in n_per_mod]
+    if idxs is None:
+        idxs = [torch.empty(int(c), dtype=torch.int32, device=dev) for c in n_per_mod]
+    if ws is None:
+        ws = workspace(lib.h3_unpack_workspace_bytes(n), dev)
+    out_arr = (_vp * 3)(*[_ptr(x) if (x is not None and x.numel()) else None for x in outs])
+    idx_arr = (_vp * 3)(*[_ptr(x) if (x is not None and x.numel()) else None for x in idxs])
+    cnt_arr = (_i32 * 3)(*[int(c) for c in n_per_mod])
+    st = lib.h3_unpack_by_modality(_ptr(o), _ptr(perm), _ptr(tags_src), n, H, D, _dt(o),
+                                   out_arr, idx_arr, cnt_arr, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "h3_unpack_by_modality")
+    return outs, idxs
+
+
+def validate_seqlens(cu_seqlens, capacity: int, stream=None) -> int:
+    """h3_validate_seqlens: returns the status code (0 = valid)."""
+    lib = load()
+    return int(lib.h3_validate_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, int(capacity),
+                                       _stream(stream)))

@@ -1,0 +1,308 @@
+// Varlen attention forward, bf16 inputs, for gfx950 (CDNA4) matrix cores.
+//
+// [P1] "生产环境下的音视频联合生成：MiniMax-H3 与 vLLM-Omni 架构解析", section 三:
+// cu_seqlens marks sub-sequences; a token's softmax runs only over keys of its
+// own sub-sequence (weight zero elsewhere).  Section 六: rows past the
+// effective length are trimmed by passing a length, never read.
+//
+// Design (FlashAttention-2 style forward, Dao 2023, laid out for CDNA4):
+//   * Work item = (head, segment, 128-row query tile).  Tiles are relative to
+//     the segment start, so no tile crosses cu_seqlens and no masked pair is
+//     ever multiplied; only a segment's last K tile masks its ragged tail.
+//   * Work order: items are head-major and split into 8 contiguous chunks, one
+//     per XCD (workgroups are dispatched round-robin over the 8 XCDs), so the
+//     query tiles running on one XCD share a head's K/V through that XCD's L2.
+//   * 4 waves per workgroup, 32 query rows per wave.  Q stays in registers as
+//     the B operand of v_mfma_f32_32x32x16_bf16.  S^T = K Q^T puts one query per
+//     lane column, so the row max / row sum are lane-local (plus one swap with
+//     lane ^ 32) and P^T feeds O^T = V^T P^T straight from the accumulator
+//     registers: K rows are read in a permuted order chosen so that each lane's
+//     S^T registers hold 8 consecutive keys, exactly the B-operand layout.
+//   * K is staged row-major and V transposed ([d][key]) in LDS, both padded;
+//     the next tile's global loads are issued before this tile's math.
+//   * Online softmax in fp32, exp2 domain: p = exp2(s * scale*log2e - m).
+#include "h3_internal.h"
+
+namespace h3 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128;     // query rows per workgroup
+constexpr int kBN = 64;      // keys per K/V tile
+constexpr int kThreads = 256;
+
+// Key held by S^T accumulator row m (0..31) of a 32-key block: rows
+// m = 8a + 4g + b read key 16(a/2) + 8g + 4(a%2) + b, so that register
+// i = 8c + e of lane group g holds key 16c + 8g + e.
+__device__ __forceinline__ int k_row_perm(int m) {
+  const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
+  return ((a >> 1) << 4) | (g << 3) | ((a & 1) << 2) | b;
+}
+
+__device__ __forceinline__ int find_segment(const int32_t* __restrict__ prefix, int n_seg, int t) {
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    int n_seg, int H, int total_rows, float scale_log2) {
+  constexpr int KP = D + 8;          // sK row pitch (elements)
+  constexpr int VP = kBN + 8;        // sV row pitch (elements)
+  constexpr int KC = D / 16;         // k-chunks of QK^T
+  constexpr int DB = D / 32;         // 32-row blocks of O^T
+  constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  constexpr int KLOAD = kBN * KCH / kThreads;            // K chunks per thread
+  constexpr int VUNITS = (kBN / 4) * (D / 8);            // 4 keys x 8 d units
+  constexpr int VLOAD = (VUNITS + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VP];
+
+  // ---- work item
+  const int T = prefix[n_seg];
+  const int64_t W = (int64_t)T * H;
+  const int64_t per = (W + 7) >> 3;
+  const int64_t jj = blockIdx.x >> 3;
+  const int64_t w = (int64_t)(blockIdx.x & 7) * per + jj;
+  if (jj >= per || w >= W) return;
+  const int h = (int)(w / T), t = (int)(w - (int64_t)h * T);
+  const int s = find_segment(prefix, n_seg, t);
+  const int seg_start = min(max(cu[s], 0), total_rows);
+  const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+  const int q0 = seg_start + (t - prefix[s]) * kBM;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int64_t rs = (int64_t)H * D;
+
+  // ---- Q fragment (B operand): lane holds Q[row r32][d = 16kc + 8g .. +8]
+  const int qrow = q0 + wave * 32 + r32;
+  bf16x8_t qf[KC];
+  if (qrow < seg_end) {
+    const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qf[kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qf[kc] = bf16x8_t{};
+  }
+
+  // ---- K/V tile staging
+  uint4 kreg[KLOAD];
+  uint4 vreg[VLOAD][4];
+  const uint16_t* kh = k + (int64_t)h * D;
+  const uint16_t* vh = v + (int64_t)h * D;
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int r = 0; r < KLOAD; ++r) {
+      const int c = tid + r * kThreads;
+      const int row = c / KCH, col = c % KCH;
+      const int key = kb + row;
+      kreg[r] = key < seg_end ? *reinterpret_cast<const uint4*>(kh + key * rs + col * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < VLOAD; ++r) {
+      const int u = tid + r * kThreads;
+      const int dc = u % (D / 8), kq = u / (D / 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kb + kq * 4 + e;
+        vreg[r][e] = (u < VUNITS && key < seg_end)
+                         ? *reinterpret_cast<const uint4*>(vh + key * rs + dc * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < KLOAD; ++r) {
+      const int c = tid + r * kThreads;
+      const int row = c / KCH, col = c % KCH;
+      *reinterpret_cast<uint4*>(sK + row * KP + col * 8) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VLOAD; ++r) {
+      const int u = tid + r * kThreads;
+      if (u < VUNITS) {
+        const int dc = u % (D / 8), kq = u / (D / 8);
+        const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[r][0]);
+        const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[r][1]);
+        const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[r][2]);
+        const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[r][3]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          // element i of each key's 8-wide chunk, keys kq*4 .. kq*4+3
+          const int wsel = i >> 1;
+          const uint32_t sh = (i & 1) ? 16 : 0;
+          const uint32_t e0 = (x0[wsel] >> sh) & 0xffff, e1 = (x1[wsel] >> sh) & 0xffff;
+          const uint32_t e2 = (x2[wsel] >> sh) & 0xffff, e3 = (x3[wsel] >> sh) & 0xffff;
+          uint2 pk;
+          pk.x = e0 | (e1 << 16);
+          pk.y = e2 | (e3 << 16);
+          *reinterpret_cast<uint2*>(sV + (dc * 8 + i) * VP + kq * 4) = pk;
+        }
+      }
+    }
+  };
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow_base = k_row_perm(r32) * KP + g * 8;
+
+  load_tile(seg_start);
+  for (int kb = seg_start; kb < seg_end; kb += kBN) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kb + kBN < seg_end) load_tile(kb + kBN);
+
+    // S^T = K Q^T for 2 blocks of 32 keys
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb] = f32x16_t{};
+      const uint16_t* kp = sK + mb * 32 * KP + krow_base;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + kc * 16);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sacc[mb], 0, 0, 0);
+      }
+    }
+    // ragged tail of the segment: keys past seg_end get -inf
+    if (kb + kBN > seg_end) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + mb * 32 + ((i >> 3) << 4) + g * 8 + (i & 7);
+          if (key >= seg_end) sacc[mb][i] = -INFINITY;
+        }
+    }
+    // online softmax (exp2 domain)
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+    bf16x8_t pk[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][c * 8 + e], scale_log2, -m_new));
+          lsum += p;
+          pk[mb][c][e] = (__bf16)p;
+        }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint16_t* vp = sV + (db * 32 + r32) * VP + g * 8;
+#pragma unroll
+      for (int kk = 0; kk < kBN / 16; ++kk) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vp + kk * 16);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk >> 1][kk & 1], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalise and store: lane holds O[row r32][d = 32db + 8a + 4g + 0..3]
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l_tot;
+  if (qrow < seg_end) {
+    uint16_t* op = o + qrow * rs + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 st;
+        const __bf16 b0 = (__bf16)(oacc[db][a * 4 + 0] * inv);
+        const __bf16 b1 = (__bf16)(oacc[db][a * 4 + 1] * inv);
+        const __bf16 b2 = (__bf16)(oacc[db][a * 4 + 2] * inv);
+        const __bf16 b3 = (__bf16)(oacc[db][a * 4 + 3] * inv);
+        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *reinterpret_cast<uint2*>(op + db * 32 + a * 8 + g * 4) = st;
+      }
+  }
+}
+
+// Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
+// segment bounds clamped to [0, total_rows]; prefix[n_seg] = 0 before the scan.
+__global__ void tile_counts_kernel(const int32_t* __restrict__ cu, int n_seg, int total_rows, int bm,
+                                   int32_t* __restrict__ prefix) {
+  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s <= n_seg; s += gridDim.x * blockDim.x) {
+    int c = 0;
+    if (s < n_seg) {
+      const int a = min(max(cu[s], 0), total_rows);
+      const int b = max(min(cu[s + 1], total_rows), a);
+      c = (b - a + bm - 1) / bm;
+    }
+    prefix[s] = c;
+  }
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int64_t total_rows, int64_t n_seg) {
+  (void)total_rows;
+  return align_up((size_t)(n_seg + 1) * 4, 256) + scan_workspace_bytes(n_seg + 1);
+}
+
+hipError_t launch_build_tiles(const int32_t* cu, int n_seg, int total_rows, int bm,
+                              int32_t* prefix, hipStream_t stream) {
+  const unsigned blocks = (unsigned)std::min<int64_t>(1024, ceil_div((int64_t)n_seg + 1, 256));
+  tile_counts_kernel<<<blocks, 256, 0, stream>>>(cu, n_seg, total_rows, bm, prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  char* scan_ws = reinterpret_cast<char*>(prefix) + align_up((size_t)(n_seg + 1) * 4, 256);
+  return exclusive_scan_i32(prefix, (int64_t)n_seg + 1, nullptr, scan_ws, stream);
+}
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
+                            const int32_t* cu, int n_seg, int max_seqlen, int total_rows,
+                            int H, int D, float scale, void* ws, hipStream_t stream) {
+  (void)max_seqlen;
+  int32_t* prefix = static_cast<int32_t*>(ws);
+  hipError_t e = launch_build_tiles(cu, n_seg, total_rows, kBM, prefix, stream);
+  if (e != hipSuccess) return e;
+  const int64_t t_max = ceil_div(total_rows, kBM) + n_seg;
+  const int64_t w_max = t_max * H;
+  const int64_t grid = 8 * ceil_div(w_max, 8);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (D == 128)
+    attn_fwd_bf16_kernel<128><<<(unsigned)grid, kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
+  else
+    attn_fwd_bf16_kernel<64><<<(unsigned)grid, kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace h3

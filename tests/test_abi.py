@@ -1,0 +1,146 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, and host-side validation returns its status before any launch.
+
+Calls here never reach a kernel launch: each one fails a host check first
+(pointers passed are never dereferenced on those paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import packed_varlen_attention_amd as h3
+from packed_varlen_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3.h")
+
+OK, NULL, DTYPE, SHAPE, SEQLENS, CAPACITY, UNSUPPORTED, HIP, WORKSPACE, ALIGN = range(10)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(h3.LIB_PATH):
+        pytest.fail("libh3.so not built; run python -m packed_varlen_attention_amd.build")
+    return h3.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in h3.version()
+    seen = set()
+    for s in range(10):
+        msg = h3.status_string(s)
+        assert msg and msg != "unknown status"
+        seen.add(msg)
+    assert len(seen) == 10
+    assert h3.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    assert lib.h3_pack_workspace_bytes(-1, 3) == 0
+    a = lib.h3_pack_workspace_bytes(58758, 2)
+    b = lib.h3_pack_workspace_bytes(114688, 675)
+    assert a > 58758 * 4 and b > 114688 * 4 + 675 * 112 * 4
+    assert lib.h3_attn_workspace_bytes(58758, 2) >= 3 * 4
+    assert lib.h3_unpack_workspace_bytes(153735) >= 153735 * 4
+
+
+def _rope(D=128):
+    import workloads as W
+    return _lib.rope_cfg(W.default_rope(D))
+
+
+P = ctypes.c_void_p(4096)       # aligned, never dereferenced on the paths below
+MIS = ctypes.c_void_p(4100)     # misaligned
+
+
+def _attn(lib, q=P, k=P, v=P, cu=P, n_seg=2, max_seqlen=64, rows=100, H=4, D=128, dt=0, scale=0.0,
+          o=P, ws=P, wsb=1 << 20):
+    return lib.h3_varlen_attn_fwd(q, k, v, cu, n_seg, max_seqlen, rows, H, D, dt, scale, o, ws, wsb, None)
+
+
+def test_attn_host_validation(lib):
+    assert _attn(lib, D=96) == UNSUPPORTED
+    assert _attn(lib, dt=7) == DTYPE
+    assert _attn(lib, H=0) == SHAPE
+    assert _attn(lib, rows=-1) == SHAPE
+    assert _attn(lib, scale=-1.0) == UNSUPPORTED
+    assert _attn(lib, scale=float("nan")) == UNSUPPORTED
+    assert _attn(lib, q=None) == NULL
+    assert _attn(lib, cu=None) == NULL
+    assert _attn(lib, o=MIS) == ALIGN
+    assert _attn(lib, ws=None) == WORKSPACE
+    assert _attn(lib, wsb=1) == WORKSPACE
+    # empty problems are a no-op success, nothing launched
+    assert _attn(lib, rows=0, q=None, k=None, v=None, o=None) == OK
+    assert _attn(lib, n_seg=0, q=None, k=None, v=None, o=None) == OK
+
+
+def _pack(lib, n=10, n_seg=2, H=2, D=128, dt=0, cap=16, rope="default", s=0.0, qs=P, qo=P, vo=P,
+          ws=P, wsb=1 << 20, cu=P):
+    cfg = _rope(D) if rope == "default" else rope
+    return lib.h3_pack_rope(qs, P, P, P, P, P, n, n_seg, H, D, dt,
+                            ctypes.byref(cfg) if cfg is not None else None, s,
+                            qo, P, vo, cap, cu, P, ws, wsb, None)
+
+
+def test_pack_host_validation(lib):
+    assert _pack(lib, cap=5) == CAPACITY
+    assert _pack(lib, n=-1) == SHAPE
+    assert _pack(lib, D=80) == UNSUPPORTED
+    assert _pack(lib, rope=None) == NULL
+    assert _pack(lib, cu=None) == NULL
+    assert _pack(lib, qs=None) == NULL
+    assert _pack(lib, qo=MIS) == ALIGN
+    assert _pack(lib, ws=None) == WORKSPACE
+    assert _pack(lib, s=float("inf")) == UNSUPPORTED
+    bad = _rope(128)
+    bad.m[1].d_t = 30          # split no longer sums to D
+    assert _pack(lib, rope=bad) == UNSUPPORTED
+    bad = _rope(128)
+    bad.m[2].base = 0.0
+    assert _pack(lib, rope=bad) == UNSUPPORTED
+    bad = _rope(128)
+    bad.m[1].d_t, bad.m[1].d_h = 31, 49   # odd slice widths
+    assert _pack(lib, rope=bad) == UNSUPPORTED
+
+
+def test_unpack_host_validation(lib):
+    out = (ctypes.c_void_p * 3)(P, P, P)
+    idx = (ctypes.c_void_p * 3)(P, P, P)
+    cnt = (ctypes.c_int32 * 3)(3, 3, 3)
+    f = lib.h3_unpack_by_modality
+    assert f(P, P, P, 8, 2, 128, 0, out, idx, cnt, P, 1 << 20, None) == SHAPE      # 9 > 8 tokens
+    cnt = (ctypes.c_int32 * 3)(3, 3, 2)
+    assert f(P, P, P, 8, 2, 128, 0, None, idx, cnt, P, 1 << 20, None) == NULL
+    assert f(None, P, P, 8, 2, 128, 0, out, idx, cnt, P, 1 << 20, None) == NULL
+    assert f(P, P, P, 8, 2, 128, 0, out, idx, cnt, P, 1, None) == WORKSPACE
+    out2 = (ctypes.c_void_p * 3)(P, MIS, P)
+    assert f(P, P, P, 8, 2, 128, 0, out2, idx, cnt, P, 1 << 20, None) == ALIGN
+    assert f(P, P, P, 8, 2, 96, 0, out, idx, cnt, P, 1 << 20, None) == UNSUPPORTED
+
+
+def test_validate_seqlens_host_checks(lib):
+    assert lib.h3_validate_seqlens(None, 2, 10, None) == NULL
+    assert lib.h3_validate_seqlens(P, -1, 10, None) == SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,230 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Element-by-element at sizes the oracle finishes in seconds (several tiles and
+ragged tails); sampled rows at the full workload sizes, in the same launch
+configuration bench.py times; integers bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_varlen_attention_amd as h3
+import workloads as W
+from gpu_common import assert_close, device_inputs, f64, run_path, sample_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _oracle_full(wl, q, k, v, heads=None):
+    """The oracle's whole path; `heads` restricts it to some heads (each head
+    is independent), to bound host time and memory at large sizes."""
+    if heads is not None:
+        q, k, v = q[:, heads], k[:, heads], v[:, heads]
+    return oracle.run(W.to_f64(q), W.to_f64(k), W.to_f64(v), wl.tags, wl.pos, wl.seg, wl.n_seg,
+                      wl.rope, wl.time_offset)
+
+
+def _check_full(wl, g, r, stagewise=True, heads=None):
+    n = wl.n
+    hs = slice(None) if heads is None else heads
+    assert g["cu"].cpu().numpy().tolist() == r["cu"].tolist()
+    assert np.array_equal(g["perm"][:n].cpu().numpy(), r["perm"])
+    assert_close(g["q"][:n, hs], r["q"], wl.dtype, "packed Q'")
+    assert_close(g["k"][:n, hs], r["k"], wl.dtype, "packed K'")
+    assert torch.equal(g["v"][:n, hs].cpu().double(), torch.from_numpy(r["v"]))   # exact copy
+    assert_close(g["o"][:n, hs], r["o"], wl.dtype, "O end-to-end")
+    for m in range(3):
+        assert np.array_equal(g["idxs"][m].cpu().numpy(), r["idxs"][m])
+        assert torch.equal(g["outs"][m], g["o"][g["idxs"][m].long()])       # exact gather
+    if stagewise:   # the oracle's attention on the GPU's own Q', K', V
+        ref = oracle.attention(f64(g["q"][:n, hs]), f64(g["k"][:n, hs]), f64(g["v"][:n, hs]), r["cu"])
+        assert_close(g["o"][:n, hs], ref, wl.dtype, "O stage-wise")
+    # pad rows past the effective length stay untouched (NaN prefill)
+    for key in ("q", "k", "v", "o"):
+        assert torch.isnan(g[key][n:].float()).all()
+
+
+def test_tiny_fp32_end_to_end():
+    wl = W.make_workload(0)
+    q, k, v = W.make_qkv(wl)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    r = _oracle_full(wl, q, k, v)
+    assert g["cu"].cpu().tolist() == [0, 10, 30, 45]
+    _check_full(wl, g, r)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_segments(D, dtype):
+    lengths = [1, 0, 33, 64, 65, 127, 128, 129, 300, 513, 1100]
+    wl = W.make_custom(lengths, H=3, D=D, dtype=dtype, q_scale=0.5 if dtype == "bf16" else 1.0,
+                       time_offset=17.0)
+    q, k, v = W.make_qkv(wl, seed=77)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    r = _oracle_full(wl, q, k, v)
+    _check_full(wl, g, r)
+
+
+def test_medium_8527_tokens_full():
+    wl = W.make_workload(1)
+    q, k, v = W.make_qkv(wl)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    r = _oracle_full(wl, q, k, v)
+    _check_full(wl, g, r, stagewise=False)
+    heads = [0, 11, 23]
+    ref = oracle.attention(f64(g["q"][:wl.n, heads]), f64(g["k"][:wl.n, heads]),
+                           f64(g["v"][:wl.n, heads]), r["cu"])
+    assert_close(g["o"][:wl.n, heads], ref, "bf16", "O stage-wise, 3 heads")
+
+
+@pytest.mark.parametrize("shifted", [False, True])
+def test_window_partitions_full(shifted):
+    wl = W.make_workload(4, shifted=shifted)
+    q, k, v = W.make_qkv(wl)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    heads = [0, 9, 23]
+    r = _oracle_full(wl, q, k, v, heads)
+    _check_full(wl, g, r, heads=heads)
+    # unpack restores grid (source) order: video index of source token i is inv_perm[i]
+    inv = np.empty(wl.n, np.int64)
+    inv[r["perm"]] = np.arange(wl.n)
+    assert np.array_equal(g["idxs"][W.VIDEO].cpu().numpy(), inv)
+
+
+def _sampled_full_size(index, heads, n_random):
+    wl = W.make_workload(index)
+    q, k, v = W.make_qkv(wl)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    n = wl.n
+    cu, perm = oracle.pack(wl.seg, wl.n_seg)
+    assert np.array_equal(g["cu"].cpu().numpy(), cu)
+    assert np.array_equal(g["perm"][:n].cpu().numpy(), perm)
+    rows = sample_rows(cu, n_random=n_random, seed=index)
+    rows_d = torch.from_numpy(rows).cuda()
+    # RoPE on the sampled source rows (RoPE is per token)
+    src = perm[rows]
+    qs, ks = W.to_f64(q[src]), W.to_f64(k[src])
+    qr, kr = oracle.rope_qk(qs, ks, wl.tags[src], wl.pos[src], wl.rope, wl.time_offset)
+    assert_close(g["q"][rows_d], qr, "bf16", "packed Q' sampled rows")
+    assert_close(g["k"][rows_d], kr, "bf16", "packed K' sampled rows")
+    # attention, end to end: oracle RoPE of every token for the sampled heads
+    qh, kh, vh = W.to_f64(q[:, heads]), W.to_f64(k[:, heads]), W.to_f64(v[:, heads])
+    qrh, krh = oracle.rope_qk(qh, kh, wl.tags, wl.pos, wl.rope, wl.time_offset)
+    ref = oracle.attention_rows(qrh[perm], krh[perm], vh[perm], cu, rows)
+    got = g["o"][rows_d][:, heads]
+    assert_close(got, ref, "bf16", "O end-to-end sampled rows")
+    # attention, stage-wise on the GPU's own packed tensors
+    ref2 = oracle.attention_rows(f64(g["q"][:n, heads]), f64(g["k"][:n, heads]), f64(g["v"][:n, heads]),
+                                 cu, rows)
+    assert_close(got, ref2, "bf16", "O stage-wise sampled rows")
+    # unpack: indices bit-exact, values an exact gather, pad rows untouched
+    _, idxs = oracle.unpack(np.zeros((n, 1, 1)), perm, wl.tags)
+    for m in range(3):
+        assert np.array_equal(g["idxs"][m].cpu().numpy(), idxs[m])
+        assert torch.equal(g["outs"][m], g["o"][g["idxs"][m].long()])
+    assert torch.isnan(g["o"][n:].float()).all()
+    assert torch.isfinite(g["o"][:n].float()).all()
+
+
+def test_h3_step_58758_tokens_sampled():
+    _sampled_full_size(2, heads=[0, 17, 39], n_random=48)
+
+
+def test_continuation_153735_tokens_sampled():
+    _sampled_full_size(3, heads=[0, 25], n_random=32)
+
+
+# ------------------------------------------------------------ GPU properties
+def _packed_inputs(wl, seed=5, scale=None):
+    q, k, v = W.make_qkv(wl, seed=seed)
+    if scale is not None:
+        q = (q.float() * scale).to(q.dtype)
+    return [t.cuda() for t in (q, k, v)]
+
+
+def test_segments_bit_identical_alone_and_poisoned():
+    wl = W.make_custom([300, 129, 64, 1, 700], H=2, D=128)
+    q, k, v = _packed_inputs(wl)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    cu_d = torch.from_numpy(cu).cuda()
+    o = h3.varlen_attn_fwd(q, k, v, cu_d, total_rows=wl.n)
+    o2 = h3.varlen_attn_fwd(q, k, v, cu_d, total_rows=wl.n)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)                                   # repeat run: bit-identical
+    for s in range(wl.n_seg):
+        a, b = int(cu[s]), int(cu[s + 1])
+        alone = h3.varlen_attn_fwd(q[a:b].contiguous(), k[a:b].contiguous(), v[a:b].contiguous(),
+                                   torch.tensor([0, b - a], dtype=torch.int32, device="cuda"),
+                                   total_rows=b - a)
+        assert torch.equal(alone, o[a:b])                       # packed == alone, bit for bit
+        qp, kp, vp = q.clone(), k.clone(), v.clone()
+        for t in (qp, kp, vp):
+            t[:a] = float("nan")
+            t[b:] = float("nan")
+        op = h3.varlen_attn_fwd(qp, kp, vp, cu_d, total_rows=wl.n)
+        assert torch.equal(op[a:b], o[a:b])                     # out-of-segment poison: no effect
+
+
+def test_nan_pad_rows_are_never_read():
+    wl = W.make_custom([256, 3661], H=2, D=128)
+    cap = wl.n + 58                                              # the page's 58 pad rows
+    q, k, v = _packed_inputs(wl)
+    cu_d = torch.from_numpy(oracle.pack(wl.seg, wl.n_seg)[0]).cuda()
+    pad = lambda t, val: torch.cat([t, torch.full((cap - wl.n,) + tuple(t.shape[1:]), val, dtype=t.dtype,
+                                                  device="cuda")])
+    clean = h3.varlen_attn_fwd(pad(q, 0.0), pad(k, 0.0), pad(v, 0.0), cu_d, total_rows=wl.n)
+    dirty = h3.varlen_attn_fwd(pad(q, float("nan")), pad(k, float("inf")), pad(v, float("nan")), cu_d,
+                               total_rows=wl.n)
+    torch.cuda.synchronize()
+    assert torch.equal(clean[:wl.n], dirty[:wl.n])
+    assert torch.isfinite(dirty[:wl.n].float()).all()
+
+
+@pytest.mark.parametrize("case", ["peaked", "large_logit"])
+def test_online_softmax_stress(case):
+    """Peaked softmax (Q x 4) and one key per segment with a large logit, which
+    forces the running max to move late in the segment."""
+    wl = W.make_custom([700, 129, 1000], H=2, D=128)
+    q, k, v = _packed_inputs(wl, scale=4.0 if case == "peaked" else None)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    if case == "large_logit":
+        for a, b in zip(cu[:-1], cu[1:]):
+            j = int(b) - 3
+            k[j] = (q[a:b].float().mean(0) * 20.0).to(k.dtype)
+    o = h3.varlen_attn_fwd(q, k, v, torch.from_numpy(cu).cuda(), total_rows=wl.n)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(q), f64(k), f64(v), cu)
+    assert_close(o, ref, "bf16", "O " + case)
+
+
+def test_softmax_scale_argument():
+    wl = W.make_custom([200, 77], H=2, D=64)
+    q, k, v = _packed_inputs(wl)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    o = h3.varlen_attn_fwd(q, k, v, torch.from_numpy(cu).cuda(), total_rows=wl.n, softmax_scale=0.3)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(q), f64(k), f64(v), cu, softmax_scale=0.3)
+    assert_close(o, ref, "bf16", "O scale 0.3")
+
+
+def test_empty_inputs_and_validation():
+    dev = "cuda"
+    wl = W.make_custom([0, 0], H=2, D=128)
+    e = torch.empty((0, 2, 128), dtype=torch.bfloat16, device=dev)
+    _, _, _, cu, _ = h3.pack_rope(e, e, e, torch.empty(0, dtype=torch.uint8, device=dev),
+                                  torch.empty((0, 3), dtype=torch.int32, device=dev),
+                                  torch.empty(0, dtype=torch.int32, device=dev), 2, wl.rope, 0.0,
+                                  capacity=0)
+    torch.cuda.synchronize()
+    assert cu.cpu().tolist() == [0, 0, 0]
+    z = torch.zeros((4, 2, 128), dtype=torch.bfloat16, device=dev)
+    o = torch.full_like(z, 7.0)
+    h3.varlen_attn_fwd(z, z, z, torch.zeros(3, dtype=torch.int32, device=dev), total_rows=0, o=o)
+    torch.cuda.synchronize()
+    assert (o == 7.0).all()                                       # nothing written
+    good = torch.tensor([0, 3, 3, 10], dtype=torch.int32, device=dev)
+    assert h3.validate_seqlens(good, capacity=10) == 0
+    assert h3.validate_seqlens(good, capacity=9) == 5             # H3_ERR_CAPACITY
+    assert h3.validate_seqlens(torch.tensor([0, 4, 3], dtype=torch.int32, device=dev), 10) == 4
+    assert h3.validate_seqlens(torch.tensor([1, 4], dtype=torch.int32, device=dev), 10) == 4

@@ -279,6 +279,24 @@ def make_qkv(wl: Workload, seed: Optional[int] = None, chunk_rows: int = 4096):
     return tuple(tensors)
 
 
+def make_qkv_on_device(wl: Workload, device, seed: Optional[int] = None):
+    """Seeded Q, K, V drawn directly on `device` (fast for the large
+    workloads).  Same recipe as make_qkv but with torch's device generator, so
+    the values differ from make_qkv's; they are deterministic for a seed."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed if seed is None else int(seed))
+    out_dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    tensors = []
+    for _ in range(3):
+        x = torch.randn((wl.n, wl.H, wl.D), generator=g, dtype=torch.float32, device=device)
+        if wl.q_scale != 1.0:
+            x.mul_(wl.q_scale)
+        tensors.append(x.to(out_dtype))
+        del x
+    return tuple(tensors)
+
+
 def to_f64(t) -> np.ndarray:
     """Exact upcast of a CPU torch tensor (fp32 or bf16) to a float64 array."""
     import torch
