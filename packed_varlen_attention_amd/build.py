@@ -26,6 +26,10 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results land in VGPRs unless register pressure moves them; without
+    # this, one-wave-per-SIMD kernels put every accumulator in AGPRs and copy
+    # the softmax inputs back out on every tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -5,22 +5,24 @@
 // own sub-sequence (weight zero elsewhere).  Section 六: rows past the
 // effective length are trimmed by passing a length, never read.
 //
-// Design (FlashAttention-2 style forward, Dao 2023, laid out for CDNA4):
-//   * Work item = (head, segment, 128-row query tile).  Tiles are relative to
-//     the segment start, so no tile crosses cu_seqlens and no masked pair is
-//     ever multiplied; only a segment's last K tile masks its ragged tail.
+// Common design (FlashAttention-2 style forward, Dao 2023, laid out for CDNA4):
+//   * Work item = (head, segment, query tile).  Tiles are relative to the
+//     segment start, so no tile crosses cu_seqlens and no masked pair is ever
+//     multiplied; only a segment's last K tile masks its ragged tail.
 //   * Work order: items are head-major and split into 8 contiguous chunks, one
 //     per XCD (workgroups are dispatched round-robin over the 8 XCDs), so the
 //     query tiles running on one XCD share a head's K/V through that XCD's L2.
-//   * 4 waves per workgroup, 32 query rows per wave.  Q stays in registers as
-//     the B operand of v_mfma_f32_32x32x16_bf16.  S^T = K Q^T puts one query per
-//     lane column, so the row max / row sum are lane-local (plus one swap with
-//     lane ^ 32) and P^T feeds O^T = V^T P^T straight from the accumulator
-//     registers: K rows are read in a permuted order chosen so that each lane's
-//     S^T registers hold 8 consecutive keys, exactly the B-operand layout.
-//   * K is staged row-major and V transposed ([d][key]) in LDS, both padded;
-//     the next tile's global loads are issued before this tile's math.
+//   * S is computed transposed, S^T = K Q^T with Q in registers as the B
+//     operand of v_mfma_f32_32x32x16_bf16: one query per lane column, so the
+//     row max / row sum are lane-local plus one exchange with lane ^ 32, and
+//     P^T feeds O^T = V^T P^T straight from the accumulator registers.
 //   * Online softmax in fp32, exp2 domain: p = exp2(s * scale*log2e - m).
+//
+// attn_fwd_bf16_d128_kernel (head dim 128, the performance path) is described
+// above its definition.  attn_fwd_bf16_kernel<D> is the generic path (used for
+// head dim 64): 128-row tiles, 32 rows per wave, two workgroups per CU, K rows
+// read in a permuted order so each lane's S^T registers hold 8 consecutive keys
+// (the B-operand layout), V transposed into LDS by the loading threads.
 #include "h3_internal.h"
 
 namespace h3 {
@@ -250,6 +252,256 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// D = 128 kernel: 64 query rows per wave, 256 per workgroup, one workgroup per
+// CU.  Each K / V^T operand read from LDS feeds two MFMAs (both 32-row query
+// blocks), halving LDS traffic per FLOP.  K and V tiles (64 keys x 256 B) move
+// HBM -> LDS with gfx950 direct loads (global_load_lds_dwordx4: no register
+// staging), double-buffered, one barrier per tile; the layout is row-major
+// with an XOR swizzle of the 16-byte chunks instead of padding.  V^T operands
+// come from the row-major V tile through the LDS transpose read
+// (ds_read_b64_tr_b16), so V is never transposed by ALU work.  Softmax:
+// running max only moves when a tile's max exceeds it by more than 2^8 (exact:
+// numerator and denominator share the same reference), row sums with
+// v_dot2c_f32_bf16 over the bf16 P actually fed to the PV product.
+// ---------------------------------------------------------------------------
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBM2 = 256;                 // query rows per workgroup
+constexpr int kTileBytes = 64 * 128 * 2;  // one 64-key K or V tile
+constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
+
+// K tile: chunk c of row r sits at slot c ^ (r & 15); conflict-free for the
+// 32-row b128 reads of the S^T A operand.
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+// V tile: slot c ^ {0, 6, 10, 12}[r & 3]; conflict-free for the transpose reads.
+__device__ __forceinline__ int swz_v(int row) { return (0xCA60 >> ((row & 3) << 2)) & 15; }
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    int n_seg, int H, int total_rows, float scale_log2) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];   // K0 K1 V0 V1
+
+  // ---- work item (same XCD-aware head-major order as the generic kernel)
+  const int T = prefix[n_seg];
+  const int64_t W = (int64_t)T * H;
+  const int64_t per = (W + 7) >> 3;
+  const int64_t jj = blockIdx.x >> 3;
+  const int64_t w = (int64_t)(blockIdx.x & 7) * per + jj;
+  if (jj >= per || w >= W) return;
+  const int h = (int)(w / T), t = (int)(w - (int64_t)h * T);
+  const int s = find_segment(prefix, n_seg, t);
+  const int seg_start = min(max(cu[s], 0), total_rows);
+  const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+  const int L = seg_end - seg_start;
+  const int q0 = seg_start + (t - prefix[s]) * kBM2;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int64_t rs = (int64_t)H * D;
+
+  // ---- Q fragments (B operand), two 32-row blocks per wave
+  bf16x8_t qf[2][8];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = q0 + wave * 64 + qb * 32 + r32;
+    if (qrow < seg_end) {
+      const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) qf[qb][kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) qf[qb][kc] = bf16x8_t{};
+    }
+  }
+
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
+  int voff[4];
+  {
+    const int rl = 4 * g + ((lane & 15) >> 2);
+    const int sv = swz_v(rl);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
+  }
+
+  // ---- direct HBM -> LDS loads: wave w fills tile rows 16w .. 16w+15, four
+  // rows (1 KB) per instruction; lane i writes LDS slot i, so it fetches the
+  // chunk that the swizzle places there.
+  const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
+  const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
+  int drow[4], kch[4], vch[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    drow[tt] = 16 * wave + 4 * tt + (lane >> 4);
+    kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
+    vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
+  }
+  auto issue_tile = [&](int tile_rel, int buf) {
+    char* kb_l = smem + buf * kTileBytes;
+    char* vb_l = smem + (2 + buf) * kTileBytes;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
+      const int64_t roff = (int64_t)key * rs;
+      __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
+                                       (lds_void_t*)(kb_l + (16 * wave + 4 * tt) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
+                                       (lds_void_t*)(vb_l + (16 * wave + 4 * tt) * 256), 16, 0, 0);
+    }
+  };
+
+  f32x16_t oacc[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16_t{};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto compute_tile = [&](int buf, int tile_rel) {
+    const char* kb_l = smem + buf * kTileBytes;
+    const char* vb_l = smem + (2 + buf) * kTileBytes;
+    // S^T = K Q^T, two 32-key blocks; each K operand feeds both query blocks
+    f32x16_t sacc[2][2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sacc[0][kb2] = f32x16_t{};
+      sacc[1][kb2] = f32x16_t{};
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_l + kb2 * 8192 + koff[kc]);
+        sacc[0][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kc], sacc[0][kb2], 0, 0, 0);
+        sacc[1][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kc], sacc[1][kb2], 0, 0, 0);
+      }
+    }
+    if (__builtin_expect(tile_rel + 64 > L, 0)) {   // ragged tail: keys past the end get -inf
+      __asm__ volatile("; ragged tail" ::: "memory");   // keep it a branch, not selects
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = tile_rel + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= L) {
+            sacc[0][kb2][i] = -INFINITY;
+            sacc[1][kb2][i] = -INFINITY;
+          }
+        }
+    }
+    // online softmax per query block (lane = query; lanes l and l^32 share it)
+    bf16x8_t pk[2][2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][kb2][i]);
+      mx = swap_halves_max(mx);
+      const float mcand = mx * scale_log2;
+      const bool need = mcand > m_run[qb] + kRescaleLog2;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        // Rare path.  The empty volatile asm keeps the compiler from
+        // if-converting it into an unconditional rescale of every
+        // accumulator on every tile.
+        __asm__ volatile("; rescale" ::: "memory");
+        const float mnew = need ? mcand : m_run[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        m_run[qb] = mnew;
+      }
+      const float mneg = -m_run[qb];
+      float lsum = l_run[qb];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pk[qb][kb2][c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb2][c * 8 + e], scale_log2, mneg));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2_t pp = {pk[qb][kb2][c][e], pk[qb][kb2][c][e + 1]};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+          }
+        }
+      l_run[qb] = lsum;
+    }
+    // O^T += V^T P^T; each V^T operand (two transpose reads) feeds both blocks
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char* vp = vb_l + voff[db] + (16 * kk) * 256;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][kk >> 1][kk & 1], oacc[0][db], 0, 0, 0);
+        oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[1][kk >> 1][kk & 1], oacc[1][db], 0, 0, 0);
+      }
+  };
+
+  const int ntiles = (L + 63) >> 6;
+  issue_tile(0, 0);
+  for (int j = 0; j < ntiles; j += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of tile j landed
+    __syncthreads();                      // ... and everyone's; tile j-1 fully consumed
+    if (j + 1 < ntiles) issue_tile((j + 1) * 64, 1);
+    compute_tile(0, j * 64);
+    if (j + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (j + 2 < ntiles) issue_tile((j + 2) * 64, 0);
+    compute_tile(1, (j + 1) * 64);
+  }
+
+  // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float inv = 1.f / swap_halves_sum(l_run[qb]);
+    const int qrow = q0 + wave * 64 + qb * 32 + r32;
+    if (qrow < seg_end) {
+      uint16_t* op = o + qrow * rs + (int64_t)h * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          uint2 st;
+          const __bf16 b0 = (__bf16)(oacc[qb][db][a4 * 4 + 0] * inv);
+          const __bf16 b1 = (__bf16)(oacc[qb][db][a4 * 4 + 1] * inv);
+          const __bf16 b2 = (__bf16)(oacc[qb][db][a4 * 4 + 2] * inv);
+          const __bf16 b3 = (__bf16)(oacc[qb][db][a4 * 4 + 3] * inv);
+          st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
+        }
+    }
+  }
+}
+
 // Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
 // segment bounds clamped to [0, total_rows]; prefix[n_seg] = 0 before the scan.
 __global__ void tile_counts_kernel(const int32_t* __restrict__ cu, int n_seg, int total_rows, int bm,
@@ -287,15 +539,16 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int H, int D, float scale, void* ws, hipStream_t stream) {
   (void)max_seqlen;
   int32_t* prefix = static_cast<int32_t*>(ws);
-  hipError_t e = launch_build_tiles(cu, n_seg, total_rows, kBM, prefix, stream);
+  const int bm = (D == 128) ? kBM2 : kBM;
+  hipError_t e = launch_build_tiles(cu, n_seg, total_rows, bm, prefix, stream);
   if (e != hipSuccess) return e;
-  const int64_t t_max = ceil_div(total_rows, kBM) + n_seg;
+  const int64_t t_max = ceil_div(total_rows, bm) + n_seg;
   const int64_t w_max = t_max * H;
   const int64_t grid = 8 * ceil_div(w_max, 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (D == 128)
-    attn_fwd_bf16_kernel<128><<<(unsigned)grid, kThreads, 0, stream>>>(
+    attn_fwd_bf16_d128_kernel<<<(unsigned)grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
   else
