@@ -254,16 +254,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // D = 128 kernel: 64 query rows per wave, 256 per workgroup, one workgroup per
-// CU.  Each K / V^T operand read from LDS feeds two MFMAs (both 32-row query
-// blocks), halving LDS traffic per FLOP.  K and V tiles (64 keys x 256 B) move
-// HBM -> LDS with gfx950 direct loads (global_load_lds_dwordx4: no register
-// staging), double-buffered, one barrier per tile; the layout is row-major
-// with an XOR swizzle of the 16-byte chunks instead of padding.  V^T operands
-// come from the row-major V tile through the LDS transpose read
-// (ds_read_b64_tr_b16), so V is never transposed by ALU work.  Softmax:
-// running max only moves when a tile's max exceeds it by more than 2^8 (exact:
-// numerator and denominator share the same reference), row sums with
-// v_dot2c_f32_bf16 over the bf16 P actually fed to the PV product.
+// CU.
+//   * Each K / V^T operand read from LDS feeds two MFMAs (both 32-row query
+//     blocks), halving LDS traffic per FLOP compared with 32 rows per wave.
+//   * K and V tiles (64 keys x 256 B each) move HBM -> LDS with gfx950 direct
+//     loads (global_load_lds_dwordx4, no register staging) into three rotating
+//     buffers; each tile is requested one full iteration before it is used.
+//     Rows are stored as loaded, with an XOR swizzle of the 16-byte chunks
+//     (no padding is possible: one load instruction fills 1 KB contiguously).
+//   * V^T operands come from the row-major V tile through the LDS transpose
+//     read (ds_read_b64_tr_b16): V is never transposed by ALU work.
+//   * Software pipeline: the exponentials of tile j run alongside the S MFMAs
+//     of tile j+1, and the row max of tile j+1 alongside the PV MFMAs of tile
+//     j, so the matrix cores and the vector ALU work at the same time.
+//   * O and Q live in AGPRs (MFMA accumulator / operand form); S, P and the
+//     softmax live in VGPRs.
+//   * Softmax: the running max moves only when a tile's max exceeds it by more
+//     than 2^8 (exact: numerator and denominator share the reference; p stays
+//     <= 256), row sums with v_dot2c_f32_bf16 over the bf16 P actually fed to
+//     the PV product.
 // ---------------------------------------------------------------------------
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -272,6 +281,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM2 = 256;                 // query rows per workgroup
 constexpr int kTileBytes = 64 * 128 * 2;  // one 64-key K or V tile
+constexpr int kStages = 3;                // rotating K+V tile buffers
 constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
 
 // K tile: chunk c of row r sits at slot c ^ (r & 15); conflict-free for the
@@ -289,12 +299,23 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
+template <int N>
+struct Int { static constexpr int value = N; };
+
+// QB = 32-row query blocks per wave; 8 / QB waves (512 / QB threads) per
+// workgroup.  The body is a device template called from non-template kernels,
+// so the host pass never has to instantiate it.
+template <int QB>
+__device__ __forceinline__ void attn_d128_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
     int n_seg, int H, int total_rows, float scale_log2) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];   // K0 K1 V0 V1
+  constexpr int NW = 8 / QB;               // waves per workgroup
+  constexpr int DMA_ROWS = 64 / NW;        // tile rows each wave loads per tensor
+  constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
+  // stage b: K tile at 2b * kTileBytes, V tile at (2b + 1) * kTileBytes
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStages * kTileBytes];
 
   // ---- work item (same XCD-aware head-major order as the generic kernel)
   const int T = prefix[n_seg];
@@ -314,11 +335,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
   const int g = lane >> 5, r32 = lane & 31;
   const int64_t rs = (int64_t)H * D;
 
-  // ---- Q fragments (B operand), two 32-row blocks per wave
-  bf16x8_t qf[2][8];
+  // ---- direct HBM -> LDS tile loads: wave w fills tile rows
+  // DMA_ROWS*w .. +DMA_ROWS-1, four rows (1 KB) per instruction; lane i
+  // writes LDS slot i, so it fetches the chunk that the swizzle places there.
+  const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
+  const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
+  int drow[DMA_INSTR], kch[DMA_INSTR], vch[DMA_INSTR];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = q0 + wave * 64 + qb * 32 + r32;
+  for (int tt = 0; tt < DMA_INSTR; ++tt) {
+    drow[tt] = DMA_ROWS * wave + 4 * tt + (lane >> 4);
+    kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
+    vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
+  }
+  auto issue_tile = [&](int tile_rel, int stage) __attribute__((always_inline)) {
+    char* kb_l = smem + (2 * stage) * kTileBytes;
+    char* vb_l = smem + (2 * stage + 1) * kTileBytes;
+#pragma unroll
+    for (int tt = 0; tt < DMA_INSTR; ++tt) {
+      const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
+      const int64_t roff = (int64_t)key * rs;
+      __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
+                                       (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
+                                       (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+    }
+  };
+
+  const int ntiles = (L + 63) >> 6;
+  issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(64, 1);
+
+  // ---- Q fragments (B operand), QB 32-row blocks per wave
+  bf16x8_t qf[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = q0 + (wave * QB + qb) * 32 + r32;
     if (qrow < seg_end) {
       const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
 #pragma unroll
@@ -343,86 +394,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
       voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
   }
 
-  // ---- direct HBM -> LDS loads: wave w fills tile rows 16w .. 16w+15, four
-  // rows (1 KB) per instruction; lane i writes LDS slot i, so it fetches the
-  // chunk that the swizzle places there.
-  const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
-  const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
-  int drow[4], kch[4], vch[4];
+  f32x16_t oacc[QB][4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    drow[tt] = 16 * wave + 4 * tt + (lane >> 4);
-    kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
-    vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
-  }
-  auto issue_tile = [&](int tile_rel, int buf) {
-    char* kb_l = smem + buf * kTileBytes;
-    char* vb_l = smem + (2 + buf) * kTileBytes;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
-      const int64_t roff = (int64_t)key * rs;
-      __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
-                                       (lds_void_t*)(kb_l + (16 * wave + 4 * tt) * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
-                                       (lds_void_t*)(vb_l + (16 * wave + 4 * tt) * 256), 16, 0, 0);
-    }
-  };
-
-  f32x16_t oacc[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16_t{};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l_run[qb] = 0.f;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute_tile = [&](int buf, int tile_rel) {
-    const char* kb_l = smem + buf * kTileBytes;
-    const char* vb_l = smem + (2 + buf) * kTileBytes;
-    // S^T = K Q^T, two 32-key blocks; each K operand feeds both query blocks
-    f32x16_t sacc[2][2];
+  // The pipeline works on 32-key halves of a tile: S^T for one half is
+  // sacc[query block] (16 fp32 each), P for one half is pk[qb][c] (two
+  // 16-key B operands per query block).
+  auto compute_s = [&](const char* kh_l, f32x16_t (&sacc)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[0][kb2] = f32x16_t{};
-      sacc[1][kb2] = f32x16_t{};
+    for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16_t{};
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_l + kb2 * 8192 + koff[kc]);
-        sacc[0][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kc], sacc[0][kb2], 0, 0, 0);
-        sacc[1][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kc], sacc[1][kb2], 0, 0, 0);
-      }
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kh_l + koff[kc]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kc], sacc[qb], 0, 0, 0);
     }
-    if (__builtin_expect(tile_rel + 64 > L, 0)) {   // ragged tail: keys past the end get -inf
+  };
+  // keys past the segment end get -inf (only a segment's last, ragged tile)
+  auto mask_tail = [&](f32x16_t (&sacc)[QB], int key_rel) __attribute__((always_inline)) {
+    if (__builtin_expect(key_rel + 32 > L, 0)) {
       __asm__ volatile("; ragged tail" ::: "memory");   // keep it a branch, not selects
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int i = 0; i < 16; ++i) {
+        const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= L) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = tile_rel + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= L) {
-            sacc[0][kb2][i] = -INFINITY;
-            sacc[1][kb2][i] = -INFINITY;
-          }
+          for (int qb = 0; qb < QB; ++qb) sacc[qb][i] = -INFINITY;
         }
+      }
     }
-    // online softmax per query block (lane = query; lanes l and l^32 share it)
-    bf16x8_t pk[2][2][2];
+  };
+  auto half_max = [&](const f32x16_t (&sacc)[QB], int qb) __attribute__((always_inline)) {
+    float mx = sacc[qb][0];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = sacc[qb][0][0];
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
+    return swap_halves_max(mx) * scale_log2;
+  };
+  // running-max update (rare rescale)
+  auto update_max = [&](const f32x16_t (&sacc)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][kb2][i]);
-      mx = swap_halves_max(mx);
-      const float mcand = mx * scale_log2;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mcand = half_max(sacc, qb);
       const bool need = mcand > m_run[qb] + kRescaleLog2;
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
         // Rare path.  The empty volatile asm keeps the compiler from
-        // if-converting it into an unconditional rescale of every
-        // accumulator on every tile.
+        // if-converting it into an unconditional rescale on every step.
         __asm__ volatile("; rescale" ::: "memory");
         const float mnew = need ? mcand : m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
@@ -433,56 +457,109 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
           for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
         m_run[qb] = mnew;
       }
+    }
+  };
+  // P = exp2(S * scale*log2e - m) as bf16 B operands, row sums accumulated
+  auto exp_half = [&](const f32x16_t (&sacc)[QB], bf16x8_t (&pk)[QB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m_run[qb];
       float lsum = l_run[qb];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int e = 0; e < 8; ++e)
+          pk[qb][c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][c * 8 + e], scale_log2, mneg));
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pk[qb][kb2][c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb2][c * 8 + e], scale_log2, mneg));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2_t pp = {pk[qb][kb2][c][e], pk[qb][kb2][c][e + 1]};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-          }
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2_t pp = {pk[qb][c][e], pk[qb][c][e + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
         }
+      }
       l_run[qb] = lsum;
     }
-    // O^T += V^T P^T; each V^T operand (two transpose reads) feeds both blocks
+  };
+  // O^T += V^T P^T for the 32 keys of one half; each V^T operand (two
+  // transpose reads) feeds every query block of the wave
+  auto pv_half = [&](const char* vh_l, const bf16x8_t (&pk)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char* vp = vb_l + voff[db] + (16 * kk) * 256;
+      for (int c = 0; c < 2; ++c) {
+        const char* vp = vh_l + voff[db] + (16 * c) * 256;
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][kk >> 1][kk & 1], oacc[0][db], 0, 0, 0);
-        oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[1][kk >> 1][kk & 1], oacc[1][db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][c], oacc[qb][db], 0, 0, 0);
       }
   };
+  auto k_half = [&](int stage, int half) __attribute__((always_inline)) {
+    return smem + (2 * stage) * kTileBytes + half * 8192;
+  };
+  auto v_half = [&](int stage, int half) __attribute__((always_inline)) {
+    return smem + (2 * stage + 1) * kTileBytes + half * 8192;
+  };
 
-  const int ntiles = (L + 63) >> 6;
-  issue_tile(0, 0);
-  for (int j = 0; j < ntiles; j += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of tile j landed
-    __syncthreads();                      // ... and everyone's; tile j-1 fully consumed
-    if (j + 1 < ntiles) issue_tile((j + 1) * 64, 1);
-    compute_tile(0, j * 64);
+  // ---- prologue: first half of tile 0; its max initialises the running max
+  f32x16_t scur[QB];
+  if (ntiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));   // tile 1 may be in flight
+  else __builtin_amdgcn_s_waitcnt(0x0F70);                              // vmcnt(0)
+  __syncthreads();
+  compute_s(k_half(0, 0), scur);
+  mask_tail(scur, 0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = half_max(scur, qb);
+
+  // One pipeline step: S of the next half on the matrix cores while the
+  // vector ALU exponentiates the current half, then O += V P for the current
+  // half while the next half's max is taken.
+  auto step = [&](const char* k_next, int key_next, const char* v_cur) __attribute__((always_inline)) {
+    bf16x8_t pk[QB][2];
+    f32x16_t snxt[QB];
+    exp_half(scur, pk);
+    compute_s(k_next, snxt);
+    pv_half(v_cur, pk);
+    mask_tail(snxt, key_next);
+    update_max(snxt);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) scur[qb] = snxt[qb];
+  };
+  auto final_step = [&](const char* v_cur) __attribute__((always_inline)) {
+    bf16x8_t pk[QB][2];
+    exp_half(scur, pk);
+    pv_half(v_cur, pk);
+  };
+  // tile j in stage j % 3: both halves, then the next tile's first half
+  auto tile = [&](auto phase, int j) __attribute__((always_inline)) {
+    constexpr int cur = decltype(phase)::value;
+    constexpr int nxt = (cur + 1) % kStages;
+    constexpr int dma = (cur + 2) % kStages;
+    step(k_half(cur, 1), j * 64 + 32, v_half(cur, 0));
+    if (j + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile j+1 (the only one in flight) landed
+      __syncthreads();                      // ... for every wave; tile j-1's buffer is free
+      if (j + 2 < ntiles) issue_tile((j + 2) * 64, dma);
+      step(k_half(nxt, 0), (j + 1) * 64, v_half(cur, 1));
+    } else {
+      final_step(v_half(cur, 1));
+    }
+  };
+
+  for (int j = 0; j < ntiles; j += 3) {
+    tile(Int<0>{}, j);
     if (j + 1 >= ntiles) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (j + 2 < ntiles) issue_tile((j + 2) * 64, 0);
-    compute_tile(1, (j + 1) * 64);
+    tile(Int<1>{}, j + 1);
+    if (j + 2 >= ntiles) break;
+    tile(Int<2>{}, j + 2);
   }
 
   // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3]
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.f / swap_halves_sum(l_run[qb]);
-    const int qrow = q0 + wave * 64 + qb * 32 + r32;
+    const int qrow = q0 + (wave * QB + qb) * 32 + r32;
     if (qrow < seg_end) {
       uint16_t* op = o + qrow * rs + (int64_t)h * D;
 #pragma unroll
@@ -500,6 +577,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_d128_kernel(
         }
     }
   }
+}
+
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    int n_seg, int H, int total_rows, float scale_log2) {
+  attn_d128_body<1>(q, k, v, o, cu, prefix, n_seg, H, total_rows, scale_log2);
 }
 
 // Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
@@ -548,7 +632,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (D == 128)
-    attn_fwd_bf16_d128_kernel<<<(unsigned)grid, kThreads, 0, stream>>>(
+    attn_fwd_bf16_d128_kernel<<<(unsigned)grid, 512, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
   else
