@@ -451,10 +451,17 @@ __device__ __forceinline__ void attn_d128_body(
         const float mnew = need ? mcand : m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
         l_run[qb] *= alpha;
+        // In-place multiply: the accumulators keep their registers on both
+        // sides of this branch, so the common path pays no register copies.
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) {
+            float x = oacc[qb][db][i];
+            __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+            oacc[qb][db][i] = x;
+          }
+        __asm__ volatile("s_nop 4" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
         m_run[qb] = mnew;
       }
     }
@@ -546,13 +553,34 @@ __device__ __forceinline__ void attn_d128_body(
       final_step(v_half(cur, 1));
     }
   };
+  // a tile known not to be among the last two: no exits, no tests
+  auto tile_steady = [&](auto phase, int j) __attribute__((always_inline)) {
+    constexpr int cur = decltype(phase)::value;
+    constexpr int nxt = (cur + 1) % kStages;
+    constexpr int dma = (cur + 2) % kStages;
+    step(k_half(cur, 1), j * 64 + 32, v_half(cur, 0));
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    issue_tile((j + 2) * 64, dma);
+    step(k_half(nxt, 0), (j + 1) * 64, v_half(cur, 1));
+  };
 
-  for (int j = 0; j < ntiles; j += 3) {
-    tile(Int<0>{}, j);
-    if (j + 1 >= ntiles) break;
+  // Main loop: three tiles per trip, one back-edge, so the accumulators keep
+  // their registers across the unrolled copies.  The last 1..3 tiles follow
+  // as straight-line code starting again at stage 0.
+  int j = 0;
+  for (; j + 4 < ntiles; j += 3) {
+    tile_steady(Int<0>{}, j);
+    tile_steady(Int<1>{}, j + 1);
+    tile_steady(Int<2>{}, j + 2);
+  }
+  tile(Int<0>{}, j);
+  if (j + 1 < ntiles) {
     tile(Int<1>{}, j + 1);
-    if (j + 2 >= ntiles) break;
-    tile(Int<2>{}, j + 2);
+    if (j + 2 < ntiles) {
+      tile(Int<2>{}, j + 2);
+      if (j + 3 < ntiles) tile(Int<0>{}, j + 3);
+    }
   }
 
   // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3]
