@@ -281,7 +281,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM2 = 256;                 // query rows per workgroup
 constexpr int kTileBytes = 64 * 128 * 2;  // one 64-key K or V tile
-constexpr int kStages = 3;                // rotating K+V tile buffers
+constexpr int kStages = 4;                // rotating K+V tile buffers (tiles requested kStages-2 ahead)
 constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
 
 // K tile: chunk c of row r sits at slot c ^ (r & 15); conflict-free for the
@@ -341,29 +341,52 @@ __device__ __forceinline__ void attn_d128_body(
   const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
   const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
   int drow[DMA_INSTR], kch[DMA_INSTR], vch[DMA_INSTR];
+  int64_t koff64[DMA_INSTR], voff64[DMA_INSTR];   // element offsets of this lane's chunks
 #pragma unroll
   for (int tt = 0; tt < DMA_INSTR; ++tt) {
     drow[tt] = DMA_ROWS * wave + 4 * tt + (lane >> 4);
     kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
     vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
+    koff64[tt] = (int64_t)drow[tt] * rs + kch[tt] * 8;
+    voff64[tt] = (int64_t)drow[tt] * rs + vch[tt] * 8;
   }
   auto issue_tile = [&](int tile_rel, int stage) __attribute__((always_inline)) {
     char* kb_l = smem + (2 * stage) * kTileBytes;
     char* vb_l = smem + (2 * stage + 1) * kTileBytes;
+    if (__builtin_expect(tile_rel + 64 <= L, 1)) {
+      const uint16_t* kt = kseg + (int64_t)tile_rel * rs;   // wave-uniform tile base
+      const uint16_t* vt = vseg + (int64_t)tile_rel * rs;
 #pragma unroll
-    for (int tt = 0; tt < DMA_INSTR; ++tt) {
-      const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
-      const int64_t roff = (int64_t)key * rs;
-      __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
-                                       (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
-                                       (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        __builtin_amdgcn_global_load_lds(kt + koff64[tt],
+                                         (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + voff64[tt],
+                                         (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
+        const int64_t roff = (int64_t)key * rs;
+        __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
+                                         (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
+                                         (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+      }
     }
   };
 
+  // s_waitcnt vmcnt(n * loads per tile): all but the newest n tiles landed
+  auto wait_tiles_in_flight = [&](int n) __attribute__((always_inline)) {
+    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * DMA_INSTR));
+  };
+  static_assert(kStages <= 4 && 4 * DMA_INSTR <= 15, "vmcnt encoding above assumes <= 15 loads in flight");
   const int ntiles = (L + 63) >> 6;
-  issue_tile(0, 0);
-  if (ntiles > 1) issue_tile(64, 1);
+#pragma unroll
+  for (int t0 = 0; t0 < kStages - 1; ++t0)
+    if (t0 < ntiles) issue_tile(t0 * 64, t0);
 
   // ---- Q fragments (B operand), QB 32-row blocks per wave
   bf16x8_t qf[QB][8];
@@ -511,8 +534,8 @@ __device__ __forceinline__ void attn_d128_body(
 
   // ---- prologue: first half of tile 0; its max initialises the running max
   f32x16_t scur[QB];
-  if (ntiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));   // tile 1 may be in flight
-  else __builtin_amdgcn_s_waitcnt(0x0F70);                              // vmcnt(0)
+  // tile 0 must have landed; tiles 1 .. kStages-2 may still be in flight
+  wait_tiles_in_flight(min(ntiles - 1, kStages - 2));
   __syncthreads();
   compute_s(k_half(0, 0), scur);
   mask_tail(scur, 0);
@@ -522,13 +545,15 @@ __device__ __forceinline__ void attn_d128_body(
   // One pipeline step: S of the next half on the matrix cores while the
   // vector ALU exponentiates the current half, then O += V P for the current
   // half while the next half's max is taken.
-  auto step = [&](const char* k_next, int key_next, const char* v_cur) __attribute__((always_inline)) {
+  // `ragged` is false where the next half cannot reach past the segment end
+  // (the main loop): no test there keeps the step one basic block.
+  auto step = [&](const char* k_next, int key_next, const char* v_cur, auto ragged) __attribute__((always_inline)) {
     bf16x8_t pk[QB][2];
     f32x16_t snxt[QB];
     exp_half(scur, pk);
     compute_s(k_next, snxt);
     pv_half(v_cur, pk);
-    mask_tail(snxt, key_next);
+    if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
     update_max(snxt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) scur[qb] = snxt[qb];
@@ -538,48 +563,47 @@ __device__ __forceinline__ void attn_d128_body(
     exp_half(scur, pk);
     pv_half(v_cur, pk);
   };
-  // tile j in stage j % 3: both halves, then the next tile's first half
-  auto tile = [&](auto phase, int j) __attribute__((always_inline)) {
+  // Tile j lives in stage j % kStages: its second half, then (after the
+  // barrier that frees tile j-1's stage for tile j+kStages-1) the next tile's
+  // first half.  `steady`: tile j+1 exists, so no exit paths.
+  auto tile = [&](auto phase, int j, auto steady) __attribute__((always_inline)) {
     constexpr int cur = decltype(phase)::value;
     constexpr int nxt = (cur + 1) % kStages;
-    constexpr int dma = (cur + 2) % kStages;
-    step(k_half(cur, 1), j * 64 + 32, v_half(cur, 0));
-    if (j + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile j+1 (the only one in flight) landed
-      __syncthreads();                      // ... for every wave; tile j-1's buffer is free
-      if (j + 2 < ntiles) issue_tile((j + 2) * 64, dma);
-      step(k_half(nxt, 0), (j + 1) * 64, v_half(cur, 1));
+    constexpr int dma = (cur + kStages - 1) % kStages;
+    constexpr bool is_steady = decltype(steady)::value != 0;
+    step(k_half(cur, 1), j * 64 + 32, v_half(cur, 0), Int<is_steady ? 0 : 1>{});
+    if (is_steady || j + 1 < ntiles) {
+      // tile j+1 must have landed; younger tiles may still be in flight
+      wait_tiles_in_flight(min(ntiles - 2 - j, kStages - 3));
+      __syncthreads();
+      if (j + kStages - 1 < ntiles) issue_tile((j + kStages - 1) * 64, dma);
+      step(k_half(nxt, 0), (j + 1) * 64, v_half(cur, 1), Int<is_steady ? 0 : 1>{});
     } else {
       final_step(v_half(cur, 1));
     }
   };
-  // a tile known not to be among the last two: no exits, no tests
-  auto tile_steady = [&](auto phase, int j) __attribute__((always_inline)) {
-    constexpr int cur = decltype(phase)::value;
-    constexpr int nxt = (cur + 1) % kStages;
-    constexpr int dma = (cur + 2) % kStages;
-    step(k_half(cur, 1), j * 64 + 32, v_half(cur, 0));
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    issue_tile((j + 2) * 64, dma);
-    step(k_half(nxt, 0), (j + 1) * 64, v_half(cur, 1));
-  };
 
-  // Main loop: three tiles per trip, one back-edge, so the accumulators keep
-  // their registers across the unrolled copies.  The last 1..3 tiles follow
-  // as straight-line code starting again at stage 0.
+  // Main loop: kStages tiles per trip, one back-edge, so the accumulators
+  // keep their registers across the unrolled copies.  A steady tile t also
+  // computes S for the first half of tile t+1 without the ragged-tail mask, so
+  // the loop stops while t+1 is still short of the last tile (t + 2 < ntiles).
+  // The last 2..kStages+1 tiles follow as straight-line code from stage 0.
   int j = 0;
-  for (; j + 4 < ntiles; j += 3) {
-    tile_steady(Int<0>{}, j);
-    tile_steady(Int<1>{}, j + 1);
-    tile_steady(Int<2>{}, j + 2);
+  for (; j + kStages + 1 < ntiles; j += kStages) {
+    tile(Int<0>{}, j, Int<1>{});
+    tile(Int<1>{}, j + 1, Int<1>{});
+    tile(Int<2>{}, j + 2, Int<1>{});
+    if constexpr (kStages > 3) tile(Int<3 % kStages>{}, j + 3, Int<1>{});
   }
-  tile(Int<0>{}, j);
+  tile(Int<0>{}, j, Int<0>{});
   if (j + 1 < ntiles) {
-    tile(Int<1>{}, j + 1);
+    tile(Int<1 % kStages>{}, j + 1, Int<0>{});
     if (j + 2 < ntiles) {
-      tile(Int<2>{}, j + 2);
-      if (j + 3 < ntiles) tile(Int<0>{}, j + 3);
+      tile(Int<2 % kStages>{}, j + 2, Int<0>{});
+      if (j + 3 < ntiles) {
+        tile(Int<3 % kStages>{}, j + 3, Int<0>{});
+        if (j + 4 < ntiles) tile(Int<4 % kStages>{}, j + 4, Int<0>{});
+      }
     }
   }
 

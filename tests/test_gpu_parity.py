@@ -57,7 +57,10 @@ def test_tiny_fp32_end_to_end():
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_segments(D, dtype):
-    lengths = [1, 0, 33, 64, 65, 127, 128, 129, 300, 513, 1100]
+    # every residue of the 64-key tile count mod 3 and mod 4 (the kernel's
+    # main loop is unrolled by its LDS ring size), each ragged and aligned
+    lengths = [1, 0, 33, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 320, 321,
+               383, 384, 385, 449, 450, 513, 577, 640, 641, 1100]
     wl = W.make_custom(lengths, H=3, D=D, dtype=dtype, q_scale=0.5 if dtype == "bf16" else 1.0,
                        time_offset=17.0)
     q, k, v = W.make_qkv(wl, seed=77)
