@@ -314,8 +314,11 @@ __device__ __forceinline__ void attn_d128_body(
   constexpr int NW = 8 / QB;               // waves per workgroup
   constexpr int DMA_ROWS = 64 / NW;        // tile rows each wave loads per tensor
   constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
-  // stage b: K tile at 2b * kTileBytes, V tile at (2b + 1) * kTileBytes
+  // K tiles of all stages in the low half, V tiles in the high half: every
+  // K read then fits the 16-bit LDS immediate offset, and V reads need one
+  // pre-added base.
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStages * kTileBytes];
+  constexpr int kVRegion = kStages * kTileBytes;
 
   // ---- work item (same XCD-aware head-major order as the generic kernel)
   const int T = prefix[n_seg];
@@ -331,7 +334,8 @@ __device__ __forceinline__ void attn_d128_body(
   const int L = seg_end - seg_start;
   const int q0 = seg_start + (t - prefix[s]) * kBM2;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
   const int g = lane >> 5, r32 = lane & 31;
   const int64_t rs = (int64_t)H * D;
 
@@ -351,8 +355,8 @@ __device__ __forceinline__ void attn_d128_body(
     voff64[tt] = (int64_t)drow[tt] * rs + vch[tt] * 8;
   }
   auto issue_tile = [&](int tile_rel, int stage) __attribute__((always_inline)) {
-    char* kb_l = smem + (2 * stage) * kTileBytes;
-    char* vb_l = smem + (2 * stage + 1) * kTileBytes;
+    char* kb_l = smem + stage * kTileBytes;
+    char* vb_l = smem + kVRegion + stage * kTileBytes;
     if (__builtin_expect(tile_rel + 64 <= L, 1)) {
       const uint16_t* kt = kseg + (int64_t)tile_rel * rs;   // wave-uniform tile base
       const uint16_t* vt = vseg + (int64_t)tile_rel * rs;
@@ -526,10 +530,10 @@ __device__ __forceinline__ void attn_d128_body(
       }
   };
   auto k_half = [&](int stage, int half) __attribute__((always_inline)) {
-    return smem + (2 * stage) * kTileBytes + half * 8192;
+    return smem + stage * kTileBytes + half * 8192;
   };
   auto v_half = [&](int stage, int half) __attribute__((always_inline)) {
-    return smem + (2 * stage + 1) * kTileBytes + half * 8192;
+    return smem + kVRegion + stage * kTileBytes + half * 8192;
   };
 
   // ---- prologue: first half of tile 0; its max initialises the running max
