@@ -476,7 +476,13 @@ __device__ __forceinline__ void attn_d128_body(
         // if-converting it into an unconditional rescale on every step.
         __asm__ volatile("; rescale" ::: "memory");
         const float mnew = need ? mcand : m_run[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        // The multiplies below are inline asm, which the compiler's hazard
+        // checks do not see: wait out the v_exp_f32 result (transcendental
+        // write -> VALU read) and the last PV MFMA writes of oacc (matrix
+        // result -> VALU read/write) here.  Routing alpha through the asm pins
+        // the exp before the wait.
+        __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
         l_run[qb] *= alpha;
         // In-place multiply: the accumulators keep their registers on both
         // sides of this branch, so the common path pays no register copies.
@@ -488,7 +494,7 @@ __device__ __forceinline__ void attn_d128_body(
             __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
             oacc[qb][db][i] = x;
           }
-        __asm__ volatile("s_nop 4" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
+        __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
         m_run[qb] = mnew;
       }
     }

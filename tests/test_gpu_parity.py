@@ -201,6 +201,30 @@ def test_online_softmax_stress(case):
     assert_close(o, ref, "bf16", "O " + case)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rate", [0.3, 0.04])
+def test_online_softmax_rescale_every_few_tiles(D, rate):
+    """Logits that climb along each segment by `rate` (log2 units) per key, so
+    the running max moves and the accumulators are rescaled every one
+    (rate 0.3) or every few (rate 0.04) 32-key halves, deep inside the
+    kernel's main loop; every row checked against the oracle."""
+    wl = W.make_custom([3000, 1500, 200], H=2, D=D)
+    q, k, v = W.make_qkv(wl, seed=11)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    amp = 4.0
+    qf, kf = q.float() * 0.1, k.float() * 0.1
+    qf[:, :, 0] += amp
+    ramp = rate / (D ** -0.5 * np.log2(np.e) * amp)        # k[:, :, 0] step per key
+    for a, b in zip(cu[:-1], cu[1:]):
+        kf[a:b, :, 0] += (torch.arange(b - a, dtype=torch.float32) * ramp)[:, None]
+    q, k = qf.to(q.dtype).cuda(), kf.to(k.dtype).cuda()
+    v = v.cuda()
+    o = h3.varlen_attn_fwd(q, k, v, torch.from_numpy(cu).cuda(), total_rows=wl.n)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(q), f64(k), f64(v), cu)
+    assert_close(o, ref, "bf16", "O rescale rate %g D %d" % (rate, D))
+
+
 def test_softmax_scale_argument():
     wl = W.make_custom([200, 77], H=2, D=64)
     q, k, v = _packed_inputs(wl)
