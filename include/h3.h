@@ -42,7 +42,8 @@ typedef enum {
   H3_OK = 0,
   H3_ERR_NULL = 1,         /* a required pointer is NULL */
   H3_ERR_DTYPE = 2,        /* unknown h3_dtype */
-  H3_ERR_SHAPE = 3,        /* negative or inconsistent n / n_seg / H / D / rows */
+  H3_ERR_SHAPE = 3,        /* negative or inconsistent n / n_seg / H / D / rows;
+                              H > 4096 */
   H3_ERR_SEQLENS = 4,      /* cu_seqlens not monotone, cu[0] != 0 (validate only) */
   H3_ERR_CAPACITY = 5,     /* rows do not fit the output capacity */
   H3_ERR_UNSUPPORTED = 6,  /* D not in {64, 128}, RoPE split invalid, bad scale */
@@ -119,8 +120,11 @@ h3_status h3_pack_rope(const void* q_src, const void* k_src, const void* v_src,
  *   softmax_scale: 0 -> 1/sqrt(D)
  *   o            : packed [>= total_rows][H][D] out, rows < total_rows written
  * O[i,h] = sum_{j in seg(i)} softmax_j(scale * Q[i,h].K[j,h]) V[j,h].
- * bf16: bf16 MFMA with fp32 accumulation and fp32 online softmax, P rounded
- * to bf16 for the PV product, one RNE rounding of O.  f32: fp32 throughout.
+ * bf16: bf16 MFMA with fp32 accumulation and fp32 online softmax in the
+ * exp2 domain; at D = 128 each Q element is multiplied by
+ * softmax_scale * log2(e) and rounded to bf16 once before the QK^T product;
+ * P is rounded to bf16 for the PV product; one RNE rounding of O.
+ * f32: fp32 throughout.
  * Supported D: 64 and 128.  Tiles never cross a cu_seqlens boundary, so no
  * FLOP is spent on masked pairs and each segment's output is bit-identical
  * to that segment computed alone. */

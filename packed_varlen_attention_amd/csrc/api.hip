@@ -11,12 +11,15 @@
 namespace {
 
 constexpr int32_t kMaxRows = 1 << 30;
+// Heads per row: keeps one 64-row tile of a head (64 * H * D * 2 bytes) below
+// 2^31, the reach of the attention kernels' 32-bit tile offsets.
+constexpr int32_t kMaxHeads = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 h3_status check_dims(int32_t H, int32_t D, h3_dtype dt) {
   if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
-  if (H <= 0) return H3_ERR_SHAPE;
+  if (H <= 0 || H > kMaxHeads) return H3_ERR_SHAPE;
   if (D != 64 && D != 128) return H3_ERR_UNSUPPORTED;
   return H3_OK;
 }

@@ -253,26 +253,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// D = 128 kernel: 64 query rows per wave, 256 per workgroup, one workgroup per
-// CU.
-//   * Each K / V^T operand read from LDS feeds two MFMAs (both 32-row query
-//     blocks), halving LDS traffic per FLOP compared with 32 rows per wave.
+// D = 128 kernel: 8 waves x 32 query rows = 256 rows per workgroup, one
+// workgroup per CU (two waves per SIMD).
 //   * K and V tiles (64 keys x 256 B each) move HBM -> LDS with gfx950 direct
-//     loads (global_load_lds_dwordx4, no register staging) into three rotating
-//     buffers; each tile is requested one full iteration before it is used.
-//     Rows are stored as loaded, with an XOR swizzle of the 16-byte chunks
-//     (no padding is possible: one load instruction fills 1 KB contiguously).
+//     loads (buffer_load_dwordx4 ... lds: no register staging, no vector
+//     address arithmetic: a per-tile buffer descriptor in SGPRs plus a
+//     constant per-lane offset) into a 4-stage ring; each tile is requested
+//     two tiles before it is used, one barrier per tile.  Every ring stage is
+//     its own __shared__ array, so the compiler's wait-count pass can tell the
+//     stages apart.  Rows are stored as loaded, with an XOR swizzle of the
+//     16-byte chunks (one load instruction fills 1 KB contiguously, so rows
+//     cannot be padded).
 //   * V^T operands come from the row-major V tile through the LDS transpose
 //     read (ds_read_b64_tr_b16): V is never transposed by ALU work.
-//   * Software pipeline: the exponentials of tile j run alongside the S MFMAs
-//     of tile j+1, and the row max of tile j+1 alongside the PV MFMAs of tile
-//     j, so the matrix cores and the vector ALU work at the same time.
-//   * O and Q live in AGPRs (MFMA accumulator / operand form); S, P and the
-//     softmax live in VGPRs.
-//   * Softmax: the running max moves only when a tile's max exceeds it by more
-//     than 2^8 (exact: numerator and denominator share the reference; p stays
-//     <= 256), row sums with v_dot2c_f32_bf16 over the bf16 P actually fed to
-//     the PV product.
+//   * Q is held in registers as the B operand, pre-multiplied by
+//     scale * log2(e) (one bf16 rounding of the product), so S arrives in the
+//     exp2 domain.  The first MFMA of every S chain takes its accumulator
+//     input from a register block holding -m (the running reference max), so
+//     the accumulators hold s - m and the exponential needs no subtraction.
+//   * Software pipeline over 32-key halves: the exponentials of half h run
+//     alongside the S MFMAs of half h+1, and the max check of half h+1
+//     alongside the PV MFMAs of half h.
+//   * Softmax: the reference m moves only when a half tile's scores exceed it
+//     by more than 2^8 (exact: numerator and denominator share m; p stays
+//     <= 256 otherwise).  The test is lane-local (each lane's 16 scores
+//     against 8), the exchange between the two lanes of a query only on the
+//     rare rescale.  Row sums use v_dot2c_f32_bf16 over the bf16 P that the
+//     PV product actually uses.
 // ---------------------------------------------------------------------------
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -281,8 +288,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM2 = 256;                 // query rows per workgroup
 constexpr int kTileBytes = 64 * 128 * 2;  // one 64-key K or V tile
-constexpr int kStages = 4;                // rotating K+V tile buffers (tiles requested kStages-2 ahead)
+constexpr int kStages = 4;                // ring stages (tiles requested kStages-2 ahead)
 constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
+// Buffer descriptor word 3 for raw (unformatted, unswizzled) dword access.
+constexpr int kBufferWord3 = 0x00020000;
 
 // K tile: chunk c of row r sits at slot c ^ (r & 15); conflict-free for the
 // 32-row b128 reads of the S^T A operand.
@@ -302,23 +311,23 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 template <int N>
 struct Int { static constexpr int value = N; };
 
-// QB = 32-row query blocks per wave; 8 / QB waves (512 / QB threads) per
-// workgroup.  The body is a device template called from non-template kernels,
-// so the host pass never has to instantiate it.
-template <int QB>
-__device__ __forceinline__ void attn_d128_body(
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
     int n_seg, int H, int total_rows, float scale_log2) {
   constexpr int D = 128;
-  constexpr int NW = 8 / QB;               // waves per workgroup
+  constexpr int NW = 8;                    // waves per workgroup
   constexpr int DMA_ROWS = 64 / NW;        // tile rows each wave loads per tensor
   constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
-  // K tiles of all stages in the low half, V tiles in the high half: every
-  // K read then fits the 16-bit LDS immediate offset, and V reads need one
-  // pre-added base.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStages * kTileBytes];
-  constexpr int kVRegion = kStages * kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char lk0[kTileBytes], lk1[kTileBytes], lk2[kTileBytes], lk3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lv0[kTileBytes], lv1[kTileBytes], lv2[kTileBytes], lv3[kTileBytes];
+  // stage is a compile-time constant at every call, so these fold away
+  auto k_stage = [&](int stage) __attribute__((always_inline)) -> char* {
+    return stage == 0 ? lk0 : stage == 1 ? lk1 : stage == 2 ? lk2 : lk3;
+  };
+  auto v_stage = [&](int stage) __attribute__((always_inline)) -> char* {
+    return stage == 0 ? lv0 : stage == 1 ? lv1 : stage == 2 ? lv2 : lv3;
+  };
 
   // ---- work item (same XCD-aware head-major order as the generic kernel)
   const int T = prefix[n_seg];
@@ -342,40 +351,45 @@ __device__ __forceinline__ void attn_d128_body(
   // ---- direct HBM -> LDS tile loads: wave w fills tile rows
   // DMA_ROWS*w .. +DMA_ROWS-1, four rows (1 KB) per instruction; lane i
   // writes LDS slot i, so it fetches the chunk that the swizzle places there.
+  // Byte offsets are relative to the tile's first row (< 64 rows * H*D*2 B,
+  // which the host keeps below 2^31).
   const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
   const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
   int drow[DMA_INSTR], kch[DMA_INSTR], vch[DMA_INSTR];
-  int64_t koff64[DMA_INSTR], voff64[DMA_INSTR];   // element offsets of this lane's chunks
+  uint32_t koff_dma[DMA_INSTR], voff_dma[DMA_INSTR];
 #pragma unroll
   for (int tt = 0; tt < DMA_INSTR; ++tt) {
     drow[tt] = DMA_ROWS * wave + 4 * tt + (lane >> 4);
     kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
     vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
-    koff64[tt] = (int64_t)drow[tt] * rs + kch[tt] * 8;
-    voff64[tt] = (int64_t)drow[tt] * rs + vch[tt] * 8;
+    koff_dma[tt] = (uint32_t)drow[tt] * row_bytes + (uint32_t)kch[tt] * 16u;
+    voff_dma[tt] = (uint32_t)drow[tt] * row_bytes + (uint32_t)vch[tt] * 16u;
   }
   auto issue_tile = [&](int tile_rel, int stage) __attribute__((always_inline)) {
-    char* kb_l = smem + stage * kTileBytes;
-    char* vb_l = smem + kVRegion + stage * kTileBytes;
+    char* kb_l = k_stage(stage);
+    char* vb_l = v_stage(stage);
+    const int nrec = (int)(64u * row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kseg + (int64_t)tile_rel * rs), (short)0, nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vseg + (int64_t)tile_rel * rs), (short)0, nrec, kBufferWord3);
     if (__builtin_expect(tile_rel + 64 <= L, 1)) {
-      const uint16_t* kt = kseg + (int64_t)tile_rel * rs;   // wave-uniform tile base
-      const uint16_t* vt = vseg + (int64_t)tile_rel * rs;
 #pragma unroll
       for (int tt = 0; tt < DMA_INSTR; ++tt) {
-        __builtin_amdgcn_global_load_lds(kt + koff64[tt],
-                                         (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + voff64[tt],
-                                         (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 koff_dma[tt], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 voff_dma[tt], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int tt = 0; tt < DMA_INSTR; ++tt) {
-        const int key = min(tile_rel + drow[tt], L - 1);   // ragged tail: repeat the last row
-        const int64_t roff = (int64_t)key * rs;
-        __builtin_amdgcn_global_load_lds(kseg + roff + kch[tt] * 8,
-                                         (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vseg + roff + vch[tt] * 8,
-                                         (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16, 0, 0);
+        const uint32_t row = (uint32_t)min(drow[tt], L - 1 - tile_rel);   // ragged tail: repeat the last row
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + (uint32_t)kch[tt] * 16u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + (uint32_t)vch[tt] * 16u, 0, 0, 0);
       }
     }
   };
@@ -386,24 +400,28 @@ __device__ __forceinline__ void attn_d128_body(
     else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));
     else __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * DMA_INSTR));
   };
-  static_assert(kStages <= 4 && 4 * DMA_INSTR <= 15, "vmcnt encoding above assumes <= 15 loads in flight");
+  static_assert(kStages == 4 && 4 * DMA_INSTR <= 15, "vmcnt encoding above assumes <= 15 loads in flight");
   const int ntiles = (L + 63) >> 6;
 #pragma unroll
   for (int t0 = 0; t0 < kStages - 1; ++t0)
     if (t0 < ntiles) issue_tile(t0 * 64, t0);
 
-  // ---- Q fragments (B operand), QB 32-row blocks per wave
-  bf16x8_t qf[QB][8];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + (wave * QB + qb) * 32 + r32;
+  // ---- Q fragment (B operand), times scale * log2(e): lane holds
+  // Q[row r32][d = 16kc + 8g .. +8]
+  bf16x8_t qf[8];
+  {
+    const int qrow = q0 + wave * 32 + r32;
     if (qrow < seg_end) {
       const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) qf[qb][kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+      for (int kc = 0; kc < 8; ++kc) {
+        qf[kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[kc][e] = (__bf16)((float)qf[kc][e] * scale_log2);
+      }
     } else {
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) qf[qb][kc] = bf16x8_t{};
+      for (int kc = 0; kc < 8; ++kc) qf[kc] = bf16x8_t{};
     }
   }
 
@@ -421,107 +439,96 @@ __device__ __forceinline__ void attn_d128_body(
       voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
   }
 
-  f32x16_t oacc[QB][4];
+  f32x16_t oacc[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16_t{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l_run[qb] = 0.f;
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+  float m_run = 0.f, l_run = 0.f;   // reference max (log2 units), row sum
+  f32x16_t neg_m = f32x16_t{};      // -m_run in all 16 elements: S accumulator input
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // The pipeline works on 32-key halves of a tile: S^T for one half is
-  // sacc[query block] (16 fp32 each), P for one half is pk[qb][c] (two
-  // 16-key B operands per query block).
-  auto compute_s = [&](const char* kh_l, f32x16_t (&sacc)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16_t{};
+  // S^T for one 32-key half (16 fp32 per lane, all of the lane's query),
+  // minus m when `biased`
+  auto compute_s = [&](const char* kh_l, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kh_l + koff[kc]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kc], sacc[qb], 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
+                                                     0, 0, 0);
     }
   };
   // keys past the segment end get -inf (only a segment's last, ragged tile)
-  auto mask_tail = [&](f32x16_t (&sacc)[QB], int key_rel) __attribute__((always_inline)) {
+  auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
     if (__builtin_expect(key_rel + 32 > L, 0)) {
       __asm__ volatile("; ragged tail" ::: "memory");   // keep it a branch, not selects
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= L) {
+        if (key >= L) sacc[i] = -INFINITY;
+      }
+    }
+  };
+  auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
+    float mx = sacc[0];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sacc[qb][i] = -INFINITY;
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    return mx;
+  };
+  // Rare path: a half tile's scores exceed the reference by more than 2^8.
+  // Move m to the pair's max, rescale O and l by 2^-delta, and shift the
+  // pending scores (computed against the old m) by -delta.
+  auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
+    const float mloc = lane_max(sacc);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
+      // The empty volatile asm keeps the compiler from if-converting this
+      // into an unconditional rescale on every step.
+      __asm__ volatile("; rescale" ::: "memory");
+      const float mpair = swap_halves_max(mloc);
+      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+      float alpha = __builtin_amdgcn_exp2f(-delta);
+      // The multiplies below are inline asm, which the compiler's hazard
+      // checks do not see: wait out the v_exp_f32 result (transcendental
+      // write -> VALU read) and the last PV MFMA writes of oacc (matrix
+      // result -> VALU read/write) here.  Routing alpha through the asm pins
+      // the exp before the wait.
+      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
+      l_run *= alpha;
+      // In-place multiply: the accumulators keep their registers on both
+      // sides of this branch, so the common path pays no register copies.
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = oacc[db][i];
+          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+          oacc[db][i] = x;
         }
+      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
+      m_run += delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] -= delta;
+        neg_m[i] = -m_run;
       }
     }
   };
-  auto half_max = [&](const f32x16_t (&sacc)[QB], int qb) __attribute__((always_inline)) {
-    float mx = sacc[qb][0];
+  // P = exp2(S - m) as bf16 B operands, row sums accumulated
+  auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
+    float lsum = l_run;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
-    return swap_halves_max(mx) * scale_log2;
-  };
-  // running-max update (rare rescale)
-  auto update_max = [&](const f32x16_t (&sacc)[QB]) __attribute__((always_inline)) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mcand = half_max(sacc, qb);
-      const bool need = mcand > m_run[qb] + kRescaleLog2;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-        // Rare path.  The empty volatile asm keeps the compiler from
-        // if-converting it into an unconditional rescale on every step.
-        __asm__ volatile("; rescale" ::: "memory");
-        const float mnew = need ? mcand : m_run[qb];
-        float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-        // The multiplies below are inline asm, which the compiler's hazard
-        // checks do not see: wait out the v_exp_f32 result (transcendental
-        // write -> VALU read) and the last PV MFMA writes of oacc (matrix
-        // result -> VALU read/write) here.  Routing alpha through the asm pins
-        // the exp before the wait.
-        __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
-        l_run[qb] *= alpha;
-        // In-place multiply: the accumulators keep their registers on both
-        // sides of this branch, so the common path pays no register copies.
+      for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = oacc[qb][db][i];
-            __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
-            oacc[qb][db][i] = x;
-          }
-        __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
-        m_run[qb] = mnew;
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
       }
     }
+    l_run = lsum;
   };
-  // P = exp2(S * scale*log2e - m) as bf16 B operands, row sums accumulated
-  auto exp_half = [&](const f32x16_t (&sacc)[QB], bf16x8_t (&pk)[QB][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mneg = -m_run[qb];
-      float lsum = l_run[qb];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pk[qb][c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][c * 8 + e], scale_log2, mneg));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2_t pp = {pk[qb][c][e], pk[qb][c][e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-        }
-      }
-      l_run[qb] = lsum;
-    }
-  };
-  // O^T += V^T P^T for the 32 keys of one half; each V^T operand (two
-  // transpose reads) feeds every query block of the wave
-  auto pv_half = [&](const char* vh_l, const bf16x8_t (&pk)[QB][2]) __attribute__((always_inline)) {
+  // O^T += V^T P^T for the 32 keys of one half (two transpose reads per
+  // V^T operand)
+  auto pv_half = [&](const char* vh_l, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -530,46 +537,43 @@ __device__ __forceinline__ void attn_d128_body(
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][c], oacc[qb][db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
       }
   };
-  auto k_half = [&](int stage, int half) __attribute__((always_inline)) {
-    return smem + stage * kTileBytes + half * 8192;
-  };
-  auto v_half = [&](int stage, int half) __attribute__((always_inline)) {
-    return smem + kVRegion + stage * kTileBytes + half * 8192;
-  };
+  auto k_half = [&](int stage, int half) __attribute__((always_inline)) { return k_stage(stage) + half * 8192; };
+  auto v_half = [&](int stage, int half) __attribute__((always_inline)) { return v_stage(stage) + half * 8192; };
 
-  // ---- prologue: first half of tile 0; its max initialises the running max
-  f32x16_t scur[QB];
+  // ---- prologue: first half of tile 0; its max sets the reference
+  f32x16_t scur;
   // tile 0 must have landed; tiles 1 .. kStages-2 may still be in flight
   wait_tiles_in_flight(min(ntiles - 1, kStages - 2));
   __syncthreads();
-  compute_s(k_half(0, 0), scur);
+  compute_s(k_half(0, 0), scur, false);
   mask_tail(scur, 0);
+  m_run = swap_halves_max(lane_max(scur));
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) m_run[qb] = half_max(scur, qb);
+  for (int i = 0; i < 16; ++i) {
+    scur[i] -= m_run;
+    neg_m[i] = -m_run;
+  }
 
   // One pipeline step: S of the next half on the matrix cores while the
   // vector ALU exponentiates the current half, then O += V P for the current
-  // half while the next half's max is taken.
+  // half while the next half's scores are checked against the reference.
   // `ragged` is false where the next half cannot reach past the segment end
   // (the main loop): no test there keeps the step one basic block.
   auto step = [&](const char* k_next, int key_next, const char* v_cur, auto ragged) __attribute__((always_inline)) {
-    bf16x8_t pk[QB][2];
-    f32x16_t snxt[QB];
+    bf16x8_t pk[2];
+    f32x16_t snxt;
     exp_half(scur, pk);
-    compute_s(k_next, snxt);
+    compute_s(k_next, snxt, true);
     pv_half(v_cur, pk);
     if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
     update_max(snxt);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) scur[qb] = snxt[qb];
+    scur = snxt;
   };
   auto final_step = [&](const char* v_cur) __attribute__((always_inline)) {
-    bf16x8_t pk[QB][2];
+    bf16x8_t pk[2];
     exp_half(scur, pk);
     pv_half(v_cur, pk);
   };
@@ -597,55 +601,45 @@ __device__ __forceinline__ void attn_d128_body(
   // keep their registers across the unrolled copies.  A steady tile t also
   // computes S for the first half of tile t+1 without the ragged-tail mask, so
   // the loop stops while t+1 is still short of the last tile (t + 2 < ntiles).
-  // The last 2..kStages+1 tiles follow as straight-line code from stage 0.
+  // The last 1..kStages+1 tiles follow as straight-line code from stage 0.
   int j = 0;
   for (; j + kStages + 1 < ntiles; j += kStages) {
     tile(Int<0>{}, j, Int<1>{});
     tile(Int<1>{}, j + 1, Int<1>{});
     tile(Int<2>{}, j + 2, Int<1>{});
-    if constexpr (kStages > 3) tile(Int<3 % kStages>{}, j + 3, Int<1>{});
+    tile(Int<3>{}, j + 3, Int<1>{});
   }
   tile(Int<0>{}, j, Int<0>{});
   if (j + 1 < ntiles) {
-    tile(Int<1 % kStages>{}, j + 1, Int<0>{});
+    tile(Int<1>{}, j + 1, Int<0>{});
     if (j + 2 < ntiles) {
-      tile(Int<2 % kStages>{}, j + 2, Int<0>{});
+      tile(Int<2>{}, j + 2, Int<0>{});
       if (j + 3 < ntiles) {
-        tile(Int<3 % kStages>{}, j + 3, Int<0>{});
-        if (j + 4 < ntiles) tile(Int<4 % kStages>{}, j + 4, Int<0>{});
+        tile(Int<3>{}, j + 3, Int<0>{});
+        if (j + 4 < ntiles) tile(Int<0>{}, j + 4, Int<0>{});
       }
     }
   }
 
   // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3]
+  const float inv = 1.f / swap_halves_sum(l_run);
+  const int qrow = q0 + wave * 32 + r32;
+  if (qrow < seg_end) {
+    uint16_t* op = o + qrow * rs + (int64_t)h * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.f / swap_halves_sum(l_run[qb]);
-    const int qrow = q0 + (wave * QB + qb) * 32 + r32;
-    if (qrow < seg_end) {
-      uint16_t* op = o + qrow * rs + (int64_t)h * D;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          uint2 st;
-          const __bf16 b0 = (__bf16)(oacc[qb][db][a4 * 4 + 0] * inv);
-          const __bf16 b1 = (__bf16)(oacc[qb][db][a4 * 4 + 1] * inv);
-          const __bf16 b2 = (__bf16)(oacc[qb][db][a4 * 4 + 2] * inv);
-          const __bf16 b3 = (__bf16)(oacc[qb][db][a4 * 4 + 3] * inv);
-          st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-          st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-          *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
-        }
-    }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 st;
+        const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
+        const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
+        const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
+        const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
+        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
+      }
   }
-}
-
-__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
-    int n_seg, int H, int total_rows, float scale_log2) {
-  attn_d128_body<1>(q, k, v, o, cu, prefix, n_seg, H, total_rows, scale_log2);
 }
 
 // Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
