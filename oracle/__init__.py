@@ -20,16 +20,27 @@ Steps and the passages they follow:
                   last cu_seqlens entry take no part)
   unpack          [P1] section 三 (output sliced by modality) and [P3]
                   window-aligned SP (token order restored)
+  sigma_schedule,
+  x0_from_velocity,
+  euler_step,
+  unpack_euler    [P1] section 四 (runtime loop stages 5-7: rectified-flow
+                  velocity to clean estimate, eta = 0 Euler step with separate
+                  video / audio sigma schedules, re-pin of anchor rows); the
+                  deployment page's 50 sigma points and flow shifts 12 / 3
 
 Pinning (tests/test_oracle.py): the page's cu_seqlens example and exact zeros,
 brute force in pure Python, torch's float64 scaled_dot_product_attention per
 segment, closed forms (L = 1, Q = 0, constant V, identical keys), the complex
 form of RoPE, the relative-position identity, time-shift invariance, and
-key-permutation invariance.  No function here is "parity unpinned".
+key-permutation invariance; for the epilogue, the straight rectified-flow
+path (one Euler step of the exact velocity lands on the path), the schedule's
+closed-form values and end points, telescoping over a whole schedule, and
+the re-pin rule.  No function here is "parity unpinned".
 """
 from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
                         attention, attention_rows, attention_weights, unpack, run,
-                        rope_qk)
+                        rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler)
 
 __all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
-           "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk"]
+           "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk",
+           "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler"]

@@ -190,6 +190,67 @@ def unpack(o, perm, tags):
 
 
 # ---------------------------------------------------------------------------
+# denoising-step epilogue ([P1] section 四, the runtime loop: stage 5 turns
+# the rectified-flow velocity into a clean estimate, stage 6 is the
+# deterministic Euler solver with eta = 0 stepping video and audio by their
+# own sigma schedules, stage 7 writes the state back and restores the pinned
+# anchor rows; the deployment page fixes 50 sigma points and flow shifts 12
+# for video and 3 for audio, the schedule itself is not printed)
+# ---------------------------------------------------------------------------
+def sigma_schedule(n_steps: int, shift: float) -> np.ndarray:
+    """n_steps noise levels from 1 down, then a final 0: float64 [n_steps+1].
+
+    Reading (the pages give only the point count and the shift): an evenly
+    spaced grid u_i = 1 - i / n_steps, i = 0 .. n_steps - 1, bent by the flow
+    shift sigma = shift * u / (1 + (shift - 1) * u), then the terminal 0 that
+    the last Euler step lands on."""
+    u = 1.0 - np.arange(n_steps, dtype=np.float64) / n_steps
+    sig = shift * u / (1.0 + (shift - 1.0) * u)
+    return np.concatenate([sig, [0.0]])
+
+
+def x0_from_velocity(z, v, sigma: float):
+    """Stage 5: with z = (1 - sigma) x0 + sigma * noise and v = noise - x0,
+    the clean estimate is x0 = z - sigma * v."""
+    return np.asarray(z, np.float64) - sigma * np.asarray(v, np.float64)
+
+
+def euler_step(z, v, sigma: float, sigma_next: float, pinned=None, anchor=None):
+    """Stages 5-7 for one modality: x0 = z - sigma v, then the eta = 0 Euler
+    step to sigma_next, z' = x0 + sigma_next * v (= z + (sigma_next - sigma) v),
+    then rows flagged in `pinned` are restored to `anchor` (left unchanged
+    when no anchor is given).  z, v, anchor: [rows, ...]; pinned: bool [rows]."""
+    z = np.asarray(z, np.float64)
+    v = np.asarray(v, np.float64)
+    out = x0_from_velocity(z, v, sigma) + sigma_next * v
+    if pinned is not None:
+        pinned = np.asarray(pinned, bool)
+        out[pinned] = z[pinned] if anchor is None else np.asarray(anchor, np.float64)[pinned]
+    return out
+
+
+def unpack_euler(o, perm, tags, z, sigma, sigma_next, pinned_src=None, anchor=None):
+    """Stage 4 slicing followed by stages 5-7 per modality: for modality m with
+    a state z[m] ([n_m, ...], tokens of tag m in source order), the velocity
+    rows are o[idx_m] (unpack) and the state steps with (sigma[m],
+    sigma_next[m]).  pinned_src: bool [n] in source order.  Returns the new
+    states (None where z[m] is None) and idx."""
+    outs, idxs = unpack(o, perm, tags)
+    tags = np.asarray(tags)
+    new = []
+    for m in (TEXT, VIDEO, AUDIO):
+        if z[m] is None:
+            new.append(None)
+            continue
+        pin = None
+        if pinned_src is not None:
+            pin = np.asarray(pinned_src, bool)[np.nonzero(tags == m)[0]]
+        new.append(euler_step(z[m], outs[m], sigma[m], sigma_next[m], pin,
+                              None if anchor is None else anchor[m]))
+    return new, idxs
+
+
+# ---------------------------------------------------------------------------
 # the whole path
 # ---------------------------------------------------------------------------
 def run(q_src, k_src, v_src, tags, pos, seg, n_seg, rope, time_offset,

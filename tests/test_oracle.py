@@ -360,3 +360,107 @@ def test_run_end_to_end_tiny():
     assert [x.shape[0] for x in r["outs"]] == [10, 20, 15]
     ref = _sdpa_per_segment(r["q"], r["k"], r["v"], r["cu"])
     assert np.max(np.abs(r["o"] - ref)) < 1e-13
+
+
+# ------------------------------------------- denoising-step epilogue (Euler)
+def test_sigma_schedule_page_values_and_closed_forms(golden):
+    sp = golden["sigma_points"]
+    ex = golden["denoise_three_step_example"]
+    for shift in (sp["video_flow_shift"], sp["audio_flow_shift"]):
+        s = oracle.sigma_schedule(sp["sigma_points"], shift)
+        assert s.shape == (sp["sigma_points"] + 1,)
+        assert s[0] == 1.0 and s[-1] == ex["last_target_sigma"]     # pure noise down to clean
+        assert np.all(np.diff(s) < 0)
+    # the three-step example: sigma_3 (max) -> sigma_2 -> sigma_1 -> 0
+    s3 = oracle.sigma_schedule(ex["steps"], 3.0)
+    assert s3.shape == (4,) and s3[0] == 1.0 and s3[-1] == 0.0
+    # shift 1 is the plain even grid
+    assert np.allclose(oracle.sigma_schedule(4, 1.0), [1.0, 0.75, 0.5, 0.25, 0.0], atol=0, rtol=0)
+    # closed forms of the shift map at u = 1/2 (4 points: u = 1, 3/4, 1/2, 1/4)
+    assert oracle.sigma_schedule(4, 3.0)[2] == pytest.approx(0.75, abs=1e-15)        # 1.5 / 2
+    assert oracle.sigma_schedule(4, 12.0)[2] == pytest.approx(12.0 / 13.0, abs=1e-15)
+    assert oracle.sigma_schedule(4, 3.0)[1] == pytest.approx(9.0 / 10.0, abs=1e-15)  # 2.25 / 2.5
+    # a larger shift keeps more noise at every interior point: video above audio
+    v = oracle.sigma_schedule(sp["sigma_points"], sp["video_flow_shift"])
+    a = oracle.sigma_schedule(sp["sigma_points"], sp["audio_flow_shift"])
+    assert np.all(v[1:-1] > a[1:-1])
+
+
+def test_euler_step_lands_on_the_straight_flow_path():
+    # z_sigma = (1 - sigma) x0 + sigma * noise, v = noise - x0: one eta = 0 step
+    # with the exact velocity reaches the path point at sigma_next.
+    rng = np.random.default_rng(5)
+    x0 = rng.standard_normal((7, 3, 16))
+    noise = rng.standard_normal((7, 3, 16))
+    v = noise - x0
+    for sig, nxt in ((1.0, 0.9), (0.6, 0.25), (0.3, 0.0)):
+        z = (1 - sig) * x0 + sig * noise
+        assert np.allclose(oracle.x0_from_velocity(z, v, sig), x0, atol=1e-13, rtol=0)
+        got = oracle.euler_step(z, v, sig, nxt)
+        assert np.allclose(got, (1 - nxt) * x0 + nxt * noise, atol=1e-13, rtol=0)
+
+
+def test_euler_whole_schedule_telescopes():
+    rng = np.random.default_rng(6)
+    x0 = rng.standard_normal((5, 8))
+    noise = rng.standard_normal((5, 8))
+    for shift in (12.0, 3.0):
+        s = oracle.sigma_schedule(50, shift)
+        # constant velocity: the steps sum to sigma_end - sigma_start = -1
+        z = noise.copy()
+        for i in range(50):
+            z = oracle.euler_step(z, x0, s[i], s[i + 1])
+        assert np.allclose(z, noise - x0, atol=1e-12, rtol=0)
+        # exact rectified-flow velocity from pure noise ends at the clean sample
+        z = noise.copy()
+        for i in range(50):
+            z = oracle.euler_step(z, noise - x0, s[i], s[i + 1])
+        assert np.allclose(z, x0, atol=1e-12, rtol=0)
+
+
+def test_euler_repin_and_degenerate_steps():
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal((6, 4))
+    v = rng.standard_normal((6, 4))
+    anchor = rng.standard_normal((6, 4))
+    pinned = np.array([True, False, False, True, False, True])
+    out = oracle.euler_step(z, v, 0.8, 0.5, pinned, anchor)
+    assert np.array_equal(out[pinned], anchor[pinned])                  # restored exactly
+    assert np.allclose(out[~pinned], z[~pinned] - 0.3 * v[~pinned], atol=1e-15, rtol=0)
+    kept = oracle.euler_step(z, v, 0.8, 0.5, pinned, None)             # no anchor: pinned rows keep z
+    assert np.array_equal(kept[pinned], z[pinned])
+    # zero step (x0 = z - sigma v, then + sigma v: equal up to one rounding)
+    assert np.allclose(oracle.euler_step(z, v, 0.4, 0.4), z, atol=1e-15, rtol=0)
+    assert np.array_equal(oracle.euler_step(z, np.zeros_like(v), 0.9, 0.1), z)   # zero velocity
+
+
+def test_unpack_euler_bruteforce():
+    # pure-Python loops over tokens against the vectorised epilogue
+    wl = W.make_workload(0)
+    rng = np.random.default_rng(8)
+    n = wl.n
+    perm = rng.permutation(n).astype(np.int32)
+    o = rng.standard_normal((n, 2, 4))
+    tags = wl.tags
+    npm = wl.n_per_modality()
+    z = [None, rng.standard_normal((npm[1], 2, 4)), rng.standard_normal((npm[2], 2, 4))]
+    anchor = [None, rng.standard_normal((npm[1], 2, 4)), rng.standard_normal((npm[2], 2, 4))]
+    pinned = rng.random(n) < 0.3
+    sig, nxt = (0.0, 0.7, 0.5), (0.0, 0.6, 0.2)
+    new, idxs = oracle.unpack_euler(o, perm, tags, z, sig, nxt, pinned, anchor)
+    inv = {int(perm[p]): p for p in range(n)}
+    for m in (1, 2):
+        k = 0
+        for i in range(n):
+            if int(tags[i]) != m:
+                continue
+            p = inv[i]
+            assert idxs[m][k] == p
+            for h in range(2):
+                for d in range(4):
+                    want = anchor[m][k, h, d] if pinned[i] else \
+                        z[m][k, h, d] + (nxt[m] - sig[m]) * o[p, h, d]
+                    assert abs(new[m][k, h, d] - want) <= 1e-15
+            k += 1
+        assert k == npm[m]
+    assert new[0] is None
