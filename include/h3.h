@@ -8,6 +8,7 @@
  *
  * Pages cited below:
  *   [P1] "生产环境下的音视频联合生成：MiniMax-H3 与 vLLM-Omni 架构解析"
+ *   [P2] "vLLM-Omni 实战：基于分布式逐层卸载（DLO）在 RTX 5090 上部署 MiniMax-H3 视频音频生成服务"
  *   [P3] "突破视频生成大模型的工程瓶颈"
  *
  * Conventions shared by every call:
@@ -155,6 +156,39 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
                                 void* const out[3], int32_t* const idx[3],
                                 const int32_t n_per_mod[3],
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Unpack + denoising-step epilogue ([P1] section 四, runtime loop stages 5-7:
+ * the rectified-flow velocity v gives the clean estimate x0 = z - sigma v; the
+ * deterministic Euler solver (eta = 0) moves the state to the next noise
+ * level, z' = x0 + sigma_next v = z + (sigma_next - sigma) v, with video and
+ * audio on their own sigma schedules; then the pinned anchor rows are
+ * restored to their original values).
+ *
+ *   o, perm, tags_src, n, H, D, dt, idx, n_per_mod: as h3_unpack_by_modality
+ *                (o is the velocity, packed; idx[m] may be NULL)
+ *   pinned_src : uint8 [n] in source order, non-zero = anchor row, or NULL
+ *   z[m]       : fp32 state [n_per_mod[m]][H][D] of modality m in source
+ *                order, updated in place; NULL = modality not stepped
+ *   anchor[m]  : fp32 [n_per_mod[m]][H][D] anchor values; pinned rows of
+ *                modality m are set to them (NULL: pinned rows keep z)
+ *   sigma[m], sigma_next[m] : host, this step's noise levels of modality m
+ * Non-pinned rows: z += (float)(sigma_next - sigma) * v, one fp32 fma per
+ * element.  Workspace: h3_unpack_workspace_bytes(n). */
+h3_status h3_unpack_euler(const void* o, const int32_t* perm, const uint8_t* tags_src,
+                          const uint8_t* pinned_src, int32_t n, int32_t H, int32_t D, h3_dtype dt,
+                          float* const z[3], const float* const anchor[3],
+                          const double sigma[3], const double sigma_next[3],
+                          int32_t* const idx[3], const int32_t n_per_mod[3],
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Noise levels of one modality's schedule, host only ([P2] "vLLM-Omni 实战：
+ * 基于分布式逐层卸载（DLO）在 RTX 5090 上部署 MiniMax-H3 视频音频生成服务",
+ * section 服务与调用: 50 sigma points, flow shift 12 for video and 3 for
+ * audio; the schedule itself is not printed).  Writes n_steps + 1 values to
+ * out: sigma_i = shift u / (1 + (shift - 1) u) with u = 1 - i / n_steps for
+ * i < n_steps, then 0.  shift > 0. */
+h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* out);
 
 /* ------------------------------------------------------------------------ */
 /* Checks cu_seqlens on the device: cu[0] == 0, non-decreasing,

@@ -7,14 +7,20 @@ The three calls of the path, each a thin wrapper over the C ABI of libh3.so
   varlen_attn_fwd(q, k, v, cu_seqlens, total_rows)   -> O
   unpack_by_modality(o, perm, tags, n_per_mod)       -> per-modality outputs and row indices
 
+and the denoising-step epilogue that can take unpack's place:
+
+  unpack_euler(o, perm, tags, n_per_mod, z, sigma, sigma_next, pinned=, anchors=)
+                                                     -> per-modality fp32 states stepped in place
+  sigma_schedule(n_steps, shift)                     -> noise levels (host only)
+
 Build the library in-tree first: ``python -m packed_varlen_attention_amd.build``.
 """
 from ._lib import (H3Error, H3_BF16, H3_F32, TEXT, VIDEO, AUDIO, LIB_PATH, SIGNATURES, load,
                    status_string, version, pack_rope, varlen_attn_fwd, unpack_by_modality,
-                   validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
+                   unpack_euler, sigma_schedule, validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
                    unpack_workspace_bytes, workspace, rope_cfg)
 
 __all__ = ["H3Error", "H3_BF16", "H3_F32", "TEXT", "VIDEO", "AUDIO", "LIB_PATH", "SIGNATURES",
            "load", "status_string", "version", "pack_rope", "varlen_attn_fwd",
-           "unpack_by_modality", "validate_seqlens", "pack_workspace_bytes",
+           "unpack_by_modality", "unpack_euler", "sigma_schedule", "validate_seqlens", "pack_workspace_bytes",
            "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg"]

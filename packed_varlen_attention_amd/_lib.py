@@ -43,6 +43,10 @@ SIGNATURES = {
     "h3_unpack_by_modality": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _c.c_int,
                                          _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_i32),
                                          _vp, _sz, _vp]),
+    "h3_unpack_euler": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _c.c_int,
+                                   _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_f64), _c.POINTER(_f64),
+                                   _c.POINTER(_vp), _c.POINTER(_i32), _vp, _sz, _vp]),
+    "h3_sigma_schedule": (_c.c_int, [_i32, _f64, _c.POINTER(_f64)]),
     "h3_validate_seqlens": (_c.c_int, [_vp, _i32, _i32, _vp]),
     "h3_status_string": (_c.c_char_p, [_c.c_int]),
     "h3_version": (_c.c_char_p, []),
@@ -237,6 +241,48 @@ def unpack_by_modality(o, perm, tags_src, n_per_mod: Sequence[int], *, outs=None
                                    out_arr, idx_arr, cnt_arr, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "h3_unpack_by_modality")
     return outs, idxs
+
+
+def unpack_euler(o, perm, tags_src, n_per_mod: Sequence[int], z, sigma, sigma_next, *,
+                 pinned=None, anchors=None, idxs=None, ws=None, stream=None):
+    """h3_unpack_euler: one eta = 0 Euler step of the per-modality fp32 states
+    z[m] (updated in place; None = not stepped) with velocity o, then re-pin.
+    Returns idxs[3]."""
+    torch = _torch()
+    lib = load()
+    n = tags_src.shape[0]
+    _, H, D = o.shape
+    dev = o.device
+    if tags_src.dtype != torch.uint8 or perm.dtype != torch.int32:
+        raise TypeError("tags_src must be uint8 and perm int32")
+    if pinned is not None and (pinned.dtype != torch.uint8 or pinned.shape[0] != n):
+        raise TypeError("pinned must be uint8 [n] in source order")
+    anchors = anchors if anchors is not None else [None, None, None]
+    for m in range(3):
+        for t in (z[m], anchors[m]):
+            if t is None:
+                continue
+            if t.dtype != torch.float32 or tuple(t.shape) != (int(n_per_mod[m]), H, D):
+                raise ValueError("z[m] and anchors[m] must be float32 [n_per_mod[m], H, D]")
+    if idxs is None:
+        idxs = [torch.empty(int(c), dtype=torch.int32, device=dev) for c in n_per_mod]
+    if ws is None:
+        ws = workspace(lib.h3_unpack_workspace_bytes(n), dev)
+    ptrs = lambda xs: (_vp * 3)(*[_ptr(x) if (x is not None and x.numel()) else None for x in xs])
+    st = lib.h3_unpack_euler(_ptr(o), _ptr(perm), _ptr(tags_src), _ptr(pinned), n, H, D, _dt(o),
+                             ptrs(z), ptrs(anchors), (_f64 * 3)(*[float(x) for x in sigma]),
+                             (_f64 * 3)(*[float(x) for x in sigma_next]), ptrs(idxs),
+                             (_i32 * 3)(*[int(c) for c in n_per_mod]), _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check(st, "h3_unpack_euler")
+    return idxs
+
+
+def sigma_schedule(n_steps: int, shift: float):
+    """h3_sigma_schedule (host only): n_steps + 1 noise levels ending at 0."""
+    out = (_f64 * (int(n_steps) + 1))() if n_steps >= 0 else (_f64 * 1)()
+    _check(load().h3_sigma_schedule(int(n_steps), float(shift), out), "h3_sigma_schedule")
+    return [float(x) for x in out]
 
 
 def validate_seqlens(cu_seqlens, capacity: int, stream=None) -> int:

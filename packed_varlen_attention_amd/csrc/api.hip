@@ -153,6 +153,50 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
                                     stream));
 }
 
+h3_status h3_unpack_euler(const void* o, const int32_t* perm, const uint8_t* tags_src,
+                          const uint8_t* pinned_src, int32_t n, int32_t H, int32_t D, h3_dtype dt,
+                          float* const z[3], const float* const anchor[3],
+                          const double sigma[3], const double sigma_next[3],
+                          int32_t* const idx[3], const int32_t n_per_mod[3],
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  h3_status st = check_dims(H, D, dt);
+  if (st != H3_OK) return st;
+  if (n < 0 || n > kMaxRows) return H3_ERR_SHAPE;
+  if (!z || !anchor || !sigma || !sigma_next || !idx || !n_per_mod) return H3_ERR_NULL;
+  h3::EulerOut eo;
+  int64_t sum = 0;
+  for (int m = 0; m < 3; ++m) {
+    if (n_per_mod[m] < 0) return H3_ERR_SHAPE;
+    sum += n_per_mod[m];
+    if (z[m] && (!isfinite(sigma[m]) || !isfinite(sigma_next[m]))) return H3_ERR_UNSUPPORTED;
+    if ((z[m] && !aligned16(z[m])) || (anchor[m] && !aligned16(anchor[m]))) return H3_ERR_ALIGN;
+    eo.z[m] = z[m];
+    eo.anchor[m] = anchor[m];
+    eo.idx[m] = idx[m];
+    eo.dsigma[m] = z[m] ? (float)(sigma_next[m] - sigma[m]) : 0.f;
+    eo.n_per_mod[m] = n_per_mod[m];
+  }
+  if (sum > n) return H3_ERR_SHAPE;
+  if (n == 0) return H3_OK;
+  if (!o || !perm || !tags_src) return H3_ERR_NULL;
+  if (!aligned16(o)) return H3_ERR_ALIGN;
+  if (!workspace || workspace_bytes < h3::unpack_workspace_bytes(n)) return H3_ERR_WORKSPACE;
+  return from_hip(h3::launch_unpack_euler(o, perm, tags_src, pinned_src, n, H, D, dt == H3_BF16, eo,
+                                          workspace, stream));
+}
+
+h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* out) {
+  if (n_steps < 1) return H3_ERR_SHAPE;
+  if (!out) return H3_ERR_NULL;
+  if (!(shift > 0.0) || !isfinite(shift)) return H3_ERR_UNSUPPORTED;
+  for (int32_t i = 0; i < n_steps; ++i) {
+    const double u = 1.0 - (double)i / (double)n_steps;
+    out[i] = shift * u / (1.0 + (shift - 1.0) * u);
+  }
+  out[n_steps] = 0.0;
+  return H3_OK;
+}
+
 h3_status h3_validate_seqlens(const int32_t* cu_seqlens, int32_t n_seg, int32_t capacity,
                               hipStream_t stream) {
   if (n_seg < 0 || capacity < 0) return H3_ERR_SHAPE;

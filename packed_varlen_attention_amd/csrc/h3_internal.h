@@ -61,5 +61,15 @@ struct UnpackOut {
 hipError_t launch_unpack(const void* o, const int32_t* perm, const uint8_t* tags, int n,
                          int H, int D, int elem_bytes, const UnpackOut& outs,
                          void* ws, hipStream_t stream);
+struct EulerOut {
+  float* z[3];              // per-modality fp32 state [n_m][H][D], updated in place (NULL: skip)
+  const float* anchor[3];   // per-modality anchor values (NULL: pinned rows keep z)
+  int32_t* idx[3];
+  float dsigma[3];          // sigma_next - sigma per modality
+  int32_t n_per_mod[3];
+};
+hipError_t launch_unpack_euler(const void* o, const int32_t* perm, const uint8_t* tags,
+                               const uint8_t* pinned, int n, int H, int D, bool bf16,
+                               const EulerOut& eo, void* ws, hipStream_t stream);
 
 }  // namespace h3

@@ -14,6 +14,15 @@
 //   3. move pass: one workgroup per packed row p: source row i = perm[p],
 //      modality m = tags[i], rank k -> idx[m][k] = p, out[m][k] = o[p]
 //      (16-byte coalesced row copy, no arithmetic on values).
+//
+// The Euler epilogue ([P1] section 四, runtime loop stages 5-7: the
+// rectified-flow velocity gives x0 = z - sigma v, the eta = 0 Euler step
+// moves the state to sigma_next, z' = z + (sigma_next - sigma) v, with video
+// and audio on their own sigma schedules, and pinned anchor rows are restored
+// afterwards) replaces pass 3 by a pass that, for packed row p of modality m
+// and rank k, reads the velocity row o[p] and updates the fp32 state row
+// z[m][k] in place, or copies anchor[m][k] into it when the token is pinned.
+// Same ranks, same coalesced 16-byte row streaming.
 #include "h3_internal.h"
 
 namespace h3 {
@@ -72,6 +81,65 @@ __global__ __launch_bounds__(kMoveThreads) void unpack_move_kernel(
   }
 }
 
+// Euler epilogue move pass.  A row is H*D elements, walked in groups of 8
+// (one 16-byte bf16 load or two fp32 loads of the velocity, two 16-byte fp32
+// loads and stores of the state).
+template <bool kBF16>
+__global__ __launch_bounds__(kMoveThreads) void unpack_euler_kernel(
+    const void* __restrict__ o, const int32_t* __restrict__ perm, const uint8_t* __restrict__ tags,
+    const uint8_t* __restrict__ pinned, int n, int nblk, int64_t row_elems,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ local_rank, EulerOut eo) {
+  const int p = blockIdx.x;
+  const int i = perm[p];
+  if (i < 0 || i >= n) return;
+  const int m = tags[i];
+  if (m > 2) return;
+  const int b = i / kRankBlock;
+  const int kk = table[m * nblk + b] - table[m * nblk] + local_rank[i];
+  if (kk < 0 || kk >= eo.n_per_mod[m]) return;
+  if (threadIdx.x == 0 && eo.idx[m]) eo.idx[m][kk] = p;
+  float* z = eo.z[m];
+  if (!z) return;
+  float4* zr = reinterpret_cast<float4*>(z + kk * row_elems);
+  const int ngrp = (int)(row_elems >> 3);
+  if (pinned && pinned[i]) {
+    // stage 7: re-pin (no anchor given: the row keeps its current value)
+    const float* an = eo.anchor[m];
+    if (!an) return;
+    const float4* ar = reinterpret_cast<const float4*>(an + kk * row_elems);
+    for (int c = threadIdx.x; c < ngrp; c += kMoveThreads) {
+      zr[2 * c] = ar[2 * c];
+      zr[2 * c + 1] = ar[2 * c + 1];
+    }
+    return;
+  }
+  const float ds = eo.dsigma[m];
+  for (int c = threadIdx.x; c < ngrp; c += kMoveThreads) {
+    float vv[8];
+    if constexpr (kBF16) {
+      const uint4 raw = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(o) + p * row_elems)[c];
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vv[2 * e] = __uint_as_float(w[e] << 16);
+        vv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const float4* vr = reinterpret_cast<const float4*>(static_cast<const float*>(o) + p * row_elems);
+      const float4 a = vr[2 * c], bq = vr[2 * c + 1];
+      vv[0] = a.x; vv[1] = a.y; vv[2] = a.z; vv[3] = a.w;
+      vv[4] = bq.x; vv[5] = bq.y; vv[6] = bq.z; vv[7] = bq.w;
+    }
+    float4 z0 = zr[2 * c], z1 = zr[2 * c + 1];
+    z0.x = fmaf(ds, vv[0], z0.x); z0.y = fmaf(ds, vv[1], z0.y);
+    z0.z = fmaf(ds, vv[2], z0.z); z0.w = fmaf(ds, vv[3], z0.w);
+    z1.x = fmaf(ds, vv[4], z1.x); z1.y = fmaf(ds, vv[5], z1.y);
+    z1.z = fmaf(ds, vv[6], z1.z); z1.w = fmaf(ds, vv[7], z1.w);
+    zr[2 * c] = z0;
+    zr[2 * c + 1] = z1;
+  }
+}
+
 }  // namespace
 
 size_t unpack_workspace_bytes(int64_t n) {
@@ -96,6 +164,29 @@ hipError_t launch_unpack(const void* o, const int32_t* perm, const uint8_t* tags
   const int64_t row_bytes = (int64_t)H * D * elem_bytes;
   unpack_move_kernel<16><<<n, kMoveThreads, 0, stream>>>(o, perm, tags, n, nblk, row_bytes, table,
                                                          local_rank, outs);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_euler(const void* o, const int32_t* perm, const uint8_t* tags,
+                               const uint8_t* pinned, int n, int H, int D, bool bf16,
+                               const EulerOut& eo, void* ws, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int nblk = (int)ceil_div(n, kRankBlock);
+  char* w = static_cast<char*>(ws);
+  int32_t* table = reinterpret_cast<int32_t*>(w);
+  w += align_up((size_t)(3 * nblk) * 4, 256);
+  int32_t* local_rank = reinterpret_cast<int32_t*>(w);
+  w += align_up((size_t)n * 4, 256);
+  unpack_rank_kernel<<<nblk, kRankBlock, 0, stream>>>(tags, n, nblk, table, local_rank);
+  hipError_t e = exclusive_scan_i32(table, 3 * (int64_t)nblk, nullptr, w, stream);
+  if (e != hipSuccess) return e;
+  const int64_t row_elems = (int64_t)H * D;
+  if (bf16)
+    unpack_euler_kernel<true><<<n, kMoveThreads, 0, stream>>>(o, perm, tags, pinned, n, nblk, row_elems,
+                                                              table, local_rank, eo);
+  else
+    unpack_euler_kernel<false><<<n, kMoveThreads, 0, stream>>>(o, perm, tags, pinned, n, nblk, row_elems,
+                                                               table, local_rank, eo);
   return hipGetLastError();
 }
 

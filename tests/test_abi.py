@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
@@ -144,3 +144,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def _euler(lib, o=P, n=8, D=128, dt=0, z=(P, P, P), an=(None, None, None), sig=(0.0, 0.9, 0.8),
+           nxt=(0.0, 0.8, 0.7), cnt=(3, 3, 2), ws=P, wsb=1 << 20):
+    zz = (ctypes.c_void_p * 3)(*z)
+    aa = (ctypes.c_void_p * 3)(*an)
+    ii = (ctypes.c_void_p * 3)(P, P, P)
+    return lib.h3_unpack_euler(o, P, P, None, n, 2, D, dt, zz, aa, (ctypes.c_double * 3)(*sig),
+                               (ctypes.c_double * 3)(*nxt), ii, (ctypes.c_int32 * 3)(*cnt), ws, wsb,
+                               None)
+
+
+def test_unpack_euler_host_validation(lib):
+    assert _euler(lib, cnt=(3, 3, 3)) == SHAPE              # 9 > 8 tokens
+    assert _euler(lib, D=96) == UNSUPPORTED
+    assert _euler(lib, sig=(0.0, float("nan"), 0.8)) == UNSUPPORTED
+    assert _euler(lib, z=(P, MIS, P)) == ALIGN
+    assert _euler(lib, an=(None, None, MIS)) == ALIGN
+    assert _euler(lib, o=None) == NULL
+    assert _euler(lib, wsb=1) == WORKSPACE
+    # nothing to do: n = 0 succeeds without touching any pointer
+    assert _euler(lib, o=None, n=0, cnt=(0, 0, 0)) == OK
+
+
+def test_sigma_schedule_host_matches_oracle(lib):
+    import numpy as np
+    import oracle
+    for n, shift in ((50, 12.0), (50, 3.0), (3, 3.0), (7, 1.0)):
+        got = h3.sigma_schedule(n, shift)
+        want = oracle.sigma_schedule(n, shift)
+        assert np.allclose(got, want, atol=1e-15, rtol=0)
+    out = (ctypes.c_double * 2)()
+    assert lib.h3_sigma_schedule(0, 3.0, out) == SHAPE
+    assert lib.h3_sigma_schedule(1, 0.0, out) == UNSUPPORTED
+    assert lib.h3_sigma_schedule(1, 3.0, None) == NULL

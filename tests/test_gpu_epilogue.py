@@ -1,0 +1,124 @@
+"""GPU parity of the denoising-step epilogue (h3_unpack_euler, through the C
+ABI) against the CPU oracle: fp32 states within max-abs 1e-5, pinned rows
+and row indices bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_varlen_attention_amd as h3
+import workloads as W
+from gpu_common import F32_MAX_ABS, device_inputs, errors, f64, run_path
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SHIFTS = (12.0, 12.0, 3.0)     # text (unused), video, audio flow shifts
+
+
+def _schedules(n_steps=50):
+    return [oracle.sigma_schedule(n_steps, s) for s in SHIFTS]
+
+
+def _run_steps(wl, o, perm, tags_d, z_d, anchors_d, pinned_d, steps, sched):
+    idxs = None
+    for i in steps:
+        sig = [sched[m][i] for m in range(3)]
+        nxt = [sched[m][i + 1] for m in range(3)]
+        idxs = h3.unpack_euler(o, perm, tags_d, wl.n_per_modality(), z_d, sig, nxt,
+                               pinned=pinned_d, anchors=anchors_d)
+    torch.cuda.synchronize()
+    return idxs
+
+
+def _oracle_steps(wl, o, perm, z, anchors, pinned, steps, sched):
+    zz = [None if x is None else x.double().numpy() for x in z]
+    an = [None if x is None else x.double().numpy() for x in anchors]
+    for i in steps:
+        sig = [sched[m][i] for m in range(3)]
+        nxt = [sched[m][i + 1] for m in range(3)]
+        zz, idxs = oracle.unpack_euler(o, perm, wl.tags, zz, sig, nxt, pinned, an)
+    return zz, idxs
+
+
+@pytest.mark.parametrize("vel_dtype", ["bf16", "f32"])
+def test_continuation_window_steps_with_repin(vel_dtype):
+    # velocity = the path's own attention output on the five-group layout
+    wl = W.make_continuation_small()
+    if vel_dtype == "f32":
+        wl = W.dataclasses.replace(wl, dtype="f32")
+    q, k, v = W.make_qkv(wl, seed=31)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    o, perm = g["o"], g["perm"]
+    z, anchors = W.make_states(wl, seed=41)
+    z[0] = None                       # text is conditioning: not stepped
+    pinned = W.pinned_rows(wl)
+    z_d = [None if x is None else x.cuda() for x in z]
+    a_d = [x.cuda() for x in anchors]
+    steps = range(0, 4)
+    sched = _schedules()
+    idxs = _run_steps(wl, o, perm, torch.from_numpy(wl.tags).cuda(), z_d, a_d,
+                      torch.from_numpy(pinned).cuda(), steps, sched)
+    want, widx = _oracle_steps(wl, f64(o[:wl.n]), perm[:wl.n].cpu().numpy(), z, anchors, pinned, steps, sched)
+    tags = wl.tags
+    for m in (1, 2):
+        assert np.array_equal(idxs[m].cpu().numpy(), widx[m])
+        max_abs, _ = errors(z_d[m], want[m])
+        assert max_abs <= F32_MAX_ABS, "modality %d: max-abs %.3e" % (m, max_abs)
+        pin_m = pinned[tags == m].astype(bool)
+        assert pin_m.any() and (~pin_m).any()
+        assert torch.equal(z_d[m][torch.from_numpy(pin_m).cuda()], a_d[m][torch.from_numpy(pin_m).cuda()])
+
+
+def test_no_anchor_keeps_pinned_rows_and_skips_null_states():
+    wl = W.make_continuation_small(H=2)
+    rng = np.random.default_rng(3)
+    o = torch.from_numpy(rng.standard_normal((wl.capacity, 2, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
+    perm = torch.arange(wl.n, dtype=torch.int32).cuda()
+    z, _ = W.make_states(wl, seed=5)
+    z_d = [x.cuda() for x in z]
+    before = [x.clone() for x in z_d]
+    pinned = W.pinned_rows(wl)
+    h3.unpack_euler(o, perm, torch.from_numpy(wl.tags).cuda(), wl.n_per_modality(),
+                    [None, z_d[1], z_d[2]], (0.0, 0.9, 0.8), (0.0, 0.7, 0.5),
+                    pinned=torch.from_numpy(pinned).cuda(), anchors=None)
+    torch.cuda.synchronize()
+    assert torch.equal(z_d[0], before[0])                      # text state untouched
+    want, _ = oracle.unpack_euler(f64(o[:wl.n]), np.arange(wl.n), wl.tags,
+                                  [None, f64(before[1]), f64(before[2])], (0.0, 0.9, 0.8), (0.0, 0.7, 0.5),
+                                  pinned, None)
+    for m in (1, 2):
+        max_abs, _ = errors(z_d[m], want[m])
+        assert max_abs <= F32_MAX_ABS
+        pin_m = torch.from_numpy(pinned[wl.tags == m].astype(bool)).cuda()
+        assert torch.equal(z_d[m][pin_m], before[m][pin_m])
+
+
+def test_h3_step_full_size_sampled_rows():
+    # the 58,758-token layout at full size (40 heads), the bench's launch shape;
+    # every row is checked against the closed form of one step
+    wl = W.make_workload(2)
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    o = (torch.randn((wl.capacity, wl.H, wl.D), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    perm = torch.arange(wl.n, dtype=torch.int32, device=dev)
+    npm = wl.n_per_modality()
+    z = [None] + [torch.randn((c, wl.H, wl.D), generator=g, device=dev) for c in npm[1:]]
+    z0 = [None] + [x.clone() for x in z[1:]]
+    sched = _schedules()
+    i = 7
+    sig = [sched[m][i] for m in range(3)]
+    nxt = [sched[m][i + 1] for m in range(3)]
+    idxs = h3.unpack_euler(o, perm, torch.from_numpy(wl.tags).to(dev), npm, z, sig, nxt)
+    torch.cuda.synchronize()
+    tags = wl.tags
+    rng = np.random.default_rng(9)
+    for m in (1, 2):
+        src = np.nonzero(tags == m)[0]
+        assert np.array_equal(idxs[m].cpu().numpy(), src)        # identity packing: idx = source row
+        ks = np.unique(np.concatenate([[0, 1, len(src) - 1], rng.integers(0, len(src), 48)]))
+        for kk in ks:
+            want = f64(z0[m][kk]) + (nxt[m] - sig[m]) * f64(o[src[kk]])
+            got = f64(z[m][kk])
+            assert np.abs(got - want).max() <= F32_MAX_ABS

@@ -301,3 +301,49 @@ def to_f64(t) -> np.ndarray:
     """Exact upcast of a CPU torch tensor (fp32 or bf16) to a float64 array."""
     import torch
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the denoising-step epilogue: per-modality latent states, anchor
+# values and the pinned-row flags.  The continuation layout's reference groups
+# (labels ending in "_ref") are the anchor rows ([P1] section 四: reference
+# frames / audio clips are pinned and restored after every update).
+# ---------------------------------------------------------------------------
+def pinned_rows(wl: Workload) -> np.ndarray:
+    """uint8 [n] in source order: 1 for tokens of a reference group."""
+    flags = []
+    for label, _m, count in wl.groups:
+        flags.append(np.full(count, 1 if label.endswith("_ref") else 0, np.uint8))
+    return np.concatenate(flags) if flags else np.zeros(0, np.uint8)
+
+
+def make_states(wl: Workload, seed: int, scale: float = 1.0):
+    """Seeded float32 N(0, 1) * scale states and anchors per modality, each
+    [n_m, H, D] (tokens of that modality in source order), as CPU torch
+    tensors: returns (z[3], anchor[3]).  One generator draws z for text,
+    video, audio, then the anchors in the same order."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    npm = wl.n_per_modality()
+    z = [torch.randn((c, wl.H, wl.D), generator=g, dtype=torch.float32) * scale for c in npm]
+    a = [torch.randn((c, wl.H, wl.D), generator=g, dtype=torch.float32) * scale for c in npm]
+    return z, a
+
+
+def make_continuation_small(H: int = 4, D: int = 128, T_ref: int = 3, T_tgt: int = 5, Hh: int = 6,
+                            W: int = 7, audio_ref: int = 13, audio_tgt: int = 37) -> Workload:
+    """The continuation window's five groups (text, audio reference, video
+    reference, audio target, video target) at a size the oracle finishes in
+    seconds; one segment, shift s = 238."""
+    b = _Builder()
+    b.text("text", 19, 0)
+    b.audio("audio_ref", audio_ref, 0)
+    b.video("video_ref", T_ref, Hh, W, 0)
+    b.audio("audio_tgt", audio_tgt, 0)
+    b.video("video_tgt", T_tgt, Hh, W, 0)
+    tags, pos, segv = b.arrays()
+    n = tags.shape[0]
+    return Workload(name="continuation_small_%dtok" % n, index=103, n=n, n_seg=1, H=H, D=D,
+                    dtype="bf16", capacity=_round_up(n, ALIGN), time_offset=238.0, q_scale=0.5,
+                    tags=tags, pos=pos, seg=segv, rope=default_rope(D), groups=b.groups)
