@@ -20,6 +20,13 @@ Steps and the passages they follow:
                   last cu_seqlens entry take no part)
   unpack          [P1] section 三 (output sliced by modality) and [P3]
                   window-aligned SP (token order restored)
+  block_layout,
+  block_means,
+  vsa_scores,
+  vsa_select,
+  vsa_attention   [P3] sparse-attention section, VSA (64-token blocks, block
+                  relevance score, top-k blocks kept, attention among the kept
+                  blocks); the gate is a stand-in (block-mean dot product)
   sigma_schedule,
   x0_from_velocity,
   euler_step,
@@ -35,12 +42,17 @@ form of RoPE, the relative-position identity, time-shift invariance, and
 key-permutation invariance; for the epilogue, the straight rectified-flow
 path (one Euler step of the exact velocity lands on the path), the schedule's
 closed-form values and end points, telescoping over a whole schedule, and
-the re-pin rule.  No function here is "parity unpinned".
+the re-pin rule; for VSA, keeping every block reduces to the pinned dense
+attention, torch's float64 SDPA with an explicit block mask, brute-force
+block means and a brute-force top-k on tiny inputs, and invariance under
+permuting keys inside a kept block.  No function here is "parity unpinned".
 """
 from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
                         attention, attention_rows, attention_weights, unpack, run,
-                        rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler)
+                        rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler,
+                        block_layout, block_means, vsa_scores, vsa_select, vsa_attention)
 
 __all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
            "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk",
-           "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler"]
+           "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler",
+           "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention"]

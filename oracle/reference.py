@@ -190,6 +190,98 @@ def unpack(o, perm, tags):
 
 
 # ---------------------------------------------------------------------------
+# VSA-style block-sparse attention ([P3] "突破视频生成大模型的工程瓶颈", sparse
+# attention section, VSA: the video tensor is cut into 4 x 4 x 4 = 64-token
+# blocks; a gate scores every block's relevance to the current query block;
+# only the top-k blocks are kept; standard attention runs among the kept
+# blocks.  The gate is learned and not described, and the top-k share of all
+# blocks is not given.)
+# Readings: blocks are 64 consecutive packed rows of one segment (the caller
+# lays the video grid out cube by cube; a segment's last block may be short);
+# the gate is the scaled dot product of block means, mean(Q rows) . mean(K
+# rows) * scale, per head; top-k per (head, query block) among the blocks of
+# the same segment, larger score first, equal scores by lower block index.
+# ---------------------------------------------------------------------------
+def block_layout(cu, block: int = 64):
+    """Blocks of every segment: returns (bstart [nb+1] packed row of each
+    block's first row (last entry = cu[-1]), bseg [nb] segment of each block,
+    bcu [n_seg+1] first block of each segment)."""
+    cu = np.asarray(cu, np.int64)
+    starts, segs, bcu = [], [], [0]
+    for s in range(cu.shape[0] - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for r in range(a, b, block):
+            starts.append(r)
+            segs.append(s)
+        bcu.append(len(starts))
+    starts.append(int(cu[-1]))
+    return np.array(starts, np.int64), np.array(segs, np.int64), np.array(bcu, np.int64)
+
+
+def block_means(x, cu, block: int = 64):
+    """Mean of the rows of every block: float64 [nb, H, D]."""
+    bstart, _, _ = block_layout(cu, block)
+    nb = bstart.shape[0] - 1
+    out = np.zeros((nb,) + tuple(x.shape[1:]), np.float64)
+    for j in range(nb):
+        out[j] = x[bstart[j]:bstart[j + 1]].mean(axis=0)
+    return out
+
+
+def vsa_scores(q, k, cu, block: int = 64, softmax_scale: Optional[float] = None):
+    """Gate scores: for every head h and pair of blocks (b, c) of one segment,
+    mean(Q_b) . mean(K_c) * scale.  Returns a list over segments of float64
+    [H, nb_s, nb_s] matrices (query block, key block), block numbers local."""
+    sc = _scale(q.shape[-1], softmax_scale)
+    qm, km = block_means(q, cu, block), block_means(k, cu, block)
+    _, _, bcu = block_layout(cu, block)
+    out = []
+    for s in range(bcu.shape[0] - 1):
+        a, b = int(bcu[s]), int(bcu[s + 1])
+        out.append(np.einsum("bhd,chd->hbc", qm[a:b], km[a:b]) * sc)
+    return out
+
+
+def vsa_select(q, k, cu, topk: int, block: int = 64, softmax_scale: Optional[float] = None):
+    """Top-k key blocks of every (head, query block): int32 [H, nb, topk] of
+    global block numbers in increasing order, -1 where the segment has fewer
+    than topk blocks."""
+    H = q.shape[1]
+    _, _, bcu = block_layout(cu, block)
+    nb = int(bcu[-1])
+    sel = np.full((H, nb, topk), -1, np.int32)
+    for s, S in enumerate(vsa_scores(q, k, cu, block, softmax_scale)):
+        a = int(bcu[s])
+        n_s = S.shape[1]
+        for h in range(H):
+            for b in range(n_s):
+                order = sorted(range(n_s), key=lambda c: (-S[h, b, c], c))[:topk]
+                chosen = sorted(order)
+                sel[h, a + b, :len(chosen)] = np.asarray(chosen, np.int64) + a
+    return sel
+
+
+def vsa_attention(q, k, v, cu, sel, block: int = 64, softmax_scale: Optional[float] = None):
+    """Every row of query block b (head h) attends to the keys of the blocks
+    listed in sel[h, b] (entries < 0 ignored), softmax over those keys only."""
+    rows, H, D = q.shape
+    sc = _scale(D, softmax_scale)
+    bstart, _, _ = block_layout(cu, block)
+    nb = bstart.shape[0] - 1
+    o = np.zeros((rows, H, D), np.float64)
+    for h in range(H):
+        for b in range(nb):
+            r0, r1 = bstart[b], bstart[b + 1]
+            keys = np.concatenate([np.arange(bstart[c], bstart[c + 1]) for c in sel[h, b] if c >= 0])
+            S = (q[r0:r1, h, :] @ k[keys, h, :].T) * sc
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P = P / P.sum(axis=1, keepdims=True)
+            o[r0:r1, h, :] = P @ v[keys, h, :]
+    return o
+
+
+# ---------------------------------------------------------------------------
 # denoising-step epilogue ([P1] section 四, the runtime loop: stage 5 turns
 # the rectified-flow velocity into a clean estimate, stage 6 is the
 # deterministic Euler solver with eta = 0 stepping video and audio by their

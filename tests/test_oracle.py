@@ -464,3 +464,105 @@ def test_unpack_euler_bruteforce():
             k += 1
         assert k == npm[m]
     assert new[0] is None
+
+
+# ------------------------------------------------ VSA block-sparse attention
+def _rand_qkv(rows, H, D, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((rows, H, D)), rng.standard_normal((rows, H, D)),
+            rng.standard_normal((rows, H, D)))
+
+
+def test_vsa_block_size_from_page_and_layout(golden):
+    vb = golden["vsa_block"]
+    assert int(np.prod(vb["block_dims"])) == vb["tokens_per_block"] == 64
+    import inspect
+    for f in (oracle.block_layout, oracle.block_means, oracle.vsa_select, oracle.vsa_attention):
+        assert inspect.signature(f).parameters["block"].default == vb["tokens_per_block"]
+    bstart, bseg, bcu = oracle.block_layout(np.array([0, 70, 70, 200, 201]))
+    assert bstart.tolist() == [0, 64, 70, 134, 198, 200, 201]
+    assert bseg.tolist() == [0, 0, 2, 2, 2, 3]
+    assert bcu.tolist() == [0, 2, 2, 5, 6]
+
+
+def test_vsa_block_means_bruteforce():
+    q, _, _ = _rand_qkv(141, 2, 3, 1)
+    cu = np.array([0, 77, 141])
+    got = oracle.block_means(q, cu)
+    bounds = [(0, 64), (64, 77), (77, 141)]
+    for j, (a, b) in enumerate(bounds):
+        for h in range(2):
+            for d in range(3):
+                acc = 0.0
+                for r in range(a, b):
+                    acc += q[r, h, d]
+                assert abs(got[j, h, d] - acc / (b - a)) <= 1e-15
+
+
+def test_vsa_select_bruteforce_with_ties():
+    q, k, _ = _rand_qkv(300, 2, 4, 2)
+    k[128:192] = k[0:64]                  # blocks 0 and 2 of segment 0 score equally
+    cu = np.array([0, 300])
+    topk = 2
+    sel = oracle.vsa_select(q, k, cu, topk)
+    nb = 5
+    bounds = [(64 * j, min(300, 64 * j + 64)) for j in range(nb)]
+    for h in range(2):
+        qm = [[sum(q[r, h, d] for r in range(a, b)) / (b - a) for d in range(4)] for a, b in bounds]
+        km = [[sum(k[r, h, d] for r in range(a, b)) / (b - a) for d in range(4)] for a, b in bounds]
+        for bq in range(nb):
+            sc = [sum(qm[bq][d] * km[c][d] for d in range(4)) / 2.0 for c in range(nb)]
+            ranked = sorted(range(nb), key=lambda c: (-sc[c], c))
+            assert sel[h, bq].tolist() == sorted(ranked[:topk])
+    # the tie: whenever block 2 is kept and block 0 is not, block 0 must have lost on score
+    S = oracle.vsa_scores(q, k, cu)[0]
+    assert np.array_equal(S[:, :, 0], S[:, :, 2])
+    for h in range(2):
+        for bq in range(nb):
+            s = sel[h, bq].tolist()
+            assert not (2 in s and 0 not in s)
+
+
+def test_vsa_keep_every_block_is_dense_attention():
+    q, k, v = _rand_qkv(333, 3, 8, 3)
+    cu = np.array([0, 50, 50, 333])
+    sel = oracle.vsa_select(q, k, cu, topk=16)
+    assert (sel[:, 0, 0] == 0).all() and (sel[:, 0, 1:] == -1).all()   # segment 0: one block
+    assert (sel[:, 1:, 5:] == -1).all() and (sel[:, 1:, :5] >= 1).all()  # segment 2: five blocks
+    got = oracle.vsa_attention(q, k, v, cu, sel)
+    assert np.allclose(got, oracle.attention(q, k, v, cu), atol=1e-13, rtol=0)
+
+
+def test_vsa_attention_matches_masked_sdpa():
+    q, k, v = _rand_qkv(260, 2, 16, 4)
+    cu = np.array([0, 260])
+    rng = np.random.default_rng(5)
+    sel = np.full((2, 5, 3), -1, np.int32)
+    for h in range(2):
+        for b in range(5):
+            n = rng.integers(1, 4)
+            sel[h, b, :n] = np.sort(rng.choice(5, size=n, replace=False))
+    got = oracle.vsa_attention(q, k, v, cu, sel)
+    bstart = [0, 64, 128, 192, 256, 260]
+    for h in range(2):
+        mask = torch.zeros((260, 260), dtype=torch.bool)
+        for b in range(5):
+            for c in sel[h, b]:
+                if c >= 0:
+                    mask[bstart[b]:bstart[b + 1], bstart[c]:bstart[c + 1]] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h])[None], torch.from_numpy(k[:, h])[None], torch.from_numpy(v[:, h])[None],
+            attn_mask=mask[None])
+        assert np.allclose(got[:, h], ref[0].numpy(), atol=1e-12, rtol=0)
+
+
+def test_vsa_key_permutation_inside_a_kept_block():
+    q, k, v = _rand_qkv(256, 2, 8, 6)
+    cu = np.array([0, 256])
+    sel = oracle.vsa_select(q, k, cu, topk=2)
+    o = oracle.vsa_attention(q, k, v, cu, sel)
+    perm = np.arange(256)
+    perm[64:128] = 64 + np.random.default_rng(7).permutation(64)
+    o2 = oracle.vsa_attention(q, k[perm], v[perm], cu, sel)     # block means and key sets unchanged
+    assert np.array_equal(oracle.vsa_select(q, k[perm], cu, topk=2), sel)
+    assert np.allclose(o, o2, atol=1e-13, rtol=0)
