@@ -158,6 +158,50 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* VSA-style block-sparse attention ([P3] sparse-attention section, VSA: the
+ * video tensor is cut into 4 x 4 x 4 = 64-token blocks; a gate scores each
+ * block's relevance to the current query; only the top-k blocks are kept and
+ * standard attention runs among them.  The pages give neither the gate nor
+ * the top-k share.)
+ *
+ * Blocks: every segment's rows [cu[s], cu[s+1]) are cut into consecutive
+ * blocks of 64 rows, the last one possibly shorter; lay the video grid out
+ * cube by cube before packing so a block is a cube.  Blocks are numbered
+ * globally in packed order; h3_vsa_blocks_bound(total_rows, n_seg) bounds
+ * their count and is the row count nb_cap of the selection array.
+ *
+ * h3_vsa_select: gate score(b, c) = mean(Q rows of b) . mean(K rows of c) *
+ * scale (fp32, per head) for blocks b, c of one segment; for every head h and
+ * query block b writes sel[h][b][0..topk) = the topk highest-scoring key
+ * blocks of b's segment (equal scores: lower block first), in increasing block
+ * order, -1 where the segment has fewer blocks.  Rows of sel past the real
+ * block count are not written.  qmean, kmean (optional, fp32
+ * [nb_cap][H][D]) receive the block means.  max_seqlen (host) must be >=
+ * every segment length: a segment with more than ceil(max_seqlen / 64)
+ * blocks is scored on its first ones only; max_seqlen <= 1,048,576.
+ *
+ * h3_vsa_attn_fwd: every row of query block b, head h, attends to the keys of
+ * the blocks listed in sel[h][b] (entries < 0 end the list; blocks outside
+ * b's segment are ignored): softmax over those keys only.  bf16, D = 128:
+ * the dense kernel's numerics (Q * scale * log2 e rounded to bf16 once, fp32
+ * accumulation and softmax, bf16 P, one RNE rounding of O).  Rows
+ * >= total_rows are neither read nor written.
+ *
+ *   q, k, v, o   : packed [>= total_rows][H][128]
+ *   sel          : int32 [H][nb_cap][topk] (device)
+ *   topk         : >= 1 */
+int32_t h3_vsa_blocks_bound(int32_t total_rows, int32_t n_seg);
+size_t h3_vsa_workspace_bytes(int32_t total_rows, int32_t n_seg, int32_t H);
+h3_status h3_vsa_select(const void* q, const void* k, const int32_t* cu_seqlens, int32_t n_seg,
+                        int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                        float softmax_scale, int32_t topk, int32_t* sel, float* qmean, float* kmean,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+h3_status h3_vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                          int32_t n_seg, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                          float softmax_scale, const int32_t* sel, int32_t topk, void* o,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Unpack + denoising-step epilogue ([P1] section 四, runtime loop stages 5-7:
  * the rectified-flow velocity v gives the clean estimate x0 = z - sigma v; the
  * deterministic Euler solver (eta = 0) moves the state to the next noise

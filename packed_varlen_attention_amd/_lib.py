@@ -47,6 +47,12 @@ SIGNATURES = {
                                    _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_f64), _c.POINTER(_f64),
                                    _c.POINTER(_vp), _c.POINTER(_i32), _vp, _sz, _vp]),
     "h3_sigma_schedule": (_c.c_int, [_i32, _f64, _c.POINTER(_f64)]),
+    "h3_vsa_blocks_bound": (_i32, [_i32, _i32]),
+    "h3_vsa_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "h3_vsa_select": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _c.c_int, _f32, _i32,
+                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "h3_vsa_attn_fwd": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _c.c_int, _f32, _vp, _i32,
+                                   _vp, _vp, _sz, _vp]),
     "h3_validate_seqlens": (_c.c_int, [_vp, _i32, _i32, _vp]),
     "h3_status_string": (_c.c_char_p, [_c.c_int]),
     "h3_version": (_c.c_char_p, []),
@@ -283,6 +289,66 @@ def sigma_schedule(n_steps: int, shift: float):
     out = (_f64 * (int(n_steps) + 1))() if n_steps >= 0 else (_f64 * 1)()
     _check(load().h3_sigma_schedule(int(n_steps), float(shift), out), "h3_sigma_schedule")
     return [float(x) for x in out]
+
+
+def vsa_blocks_bound(total_rows: int, n_seg: int) -> int:
+    """Upper bound of the number of 64-row blocks (rows of the selection)."""
+    return int(load().h3_vsa_blocks_bound(int(total_rows), int(n_seg)))
+
+
+def vsa_select(q, k, cu_seqlens, total_rows: int, topk: int, max_seqlen: int, softmax_scale: float = 0.0,
+               *, sel=None, means: bool = False, ws=None, stream=None):
+    """h3_vsa_select: top-k key blocks per (head, query block).  Returns sel
+    int32 [H, nb_cap, topk], or (sel, qmean, kmean) with means=True."""
+    torch = _torch()
+    lib = load()
+    rows, H, D = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if total_rows > rows:
+        raise ValueError("total_rows exceeds the tensors' rows")
+    n_seg = cu_seqlens.shape[0] - 1
+    nb_cap = vsa_blocks_bound(total_rows, n_seg)
+    if sel is None:
+        sel = torch.full((H, max(nb_cap, 1), int(topk)), -1, dtype=torch.int32, device=q.device)
+    qm = km = None
+    if means:
+        qm = torch.zeros((max(nb_cap, 1), H, D), dtype=torch.float32, device=q.device)
+        km = torch.zeros_like(qm)
+    if ws is None:
+        ws = workspace(lib.h3_vsa_workspace_bytes(total_rows, n_seg, H), q.device)
+    st = lib.h3_vsa_select(_ptr(q), _ptr(k), _ptr(cu_seqlens), n_seg, int(max_seqlen), int(total_rows), H, D,
+                           _dt(q), float(softmax_scale), int(topk), _ptr(sel), _ptr(qm), _ptr(km), _ptr(ws),
+                           ws.numel(), _stream(stream))
+    _check(st, "h3_vsa_select")
+    return (sel, qm, km) if means else sel
+
+
+def vsa_attn_fwd(q, k, v, cu_seqlens, total_rows: int, sel, topk: int, softmax_scale: float = 0.0, *, o=None,
+                 ws=None, stream=None):
+    """h3_vsa_attn_fwd: block-sparse attention over the blocks listed in sel."""
+    torch = _torch()
+    lib = load()
+    rows, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if cu_seqlens.dtype != torch.int32 or sel.dtype != torch.int32:
+        raise TypeError("cu_seqlens and sel must be int32")
+    n_seg = cu_seqlens.shape[0] - 1
+    nb_cap = vsa_blocks_bound(total_rows, n_seg)
+    if tuple(sel.shape) != (H, max(nb_cap, 1), int(topk)):
+        raise ValueError("sel must be [H, vsa_blocks_bound, topk]")
+    if o is None:
+        o = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(lib.h3_vsa_workspace_bytes(total_rows, n_seg, H), q.device)
+    st = lib.h3_vsa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), n_seg, int(total_rows), H, D, _dt(q),
+                             float(softmax_scale), _ptr(sel), int(topk), _ptr(o), _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check(st, "h3_vsa_attn_fwd")
+    return o
 
 
 def validate_seqlens(cu_seqlens, capacity: int, stream=None) -> int:

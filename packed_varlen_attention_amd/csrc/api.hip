@@ -197,6 +197,65 @@ h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* out) {
   return H3_OK;
 }
 
+int32_t h3_vsa_blocks_bound(int32_t total_rows, int32_t n_seg) {
+  if (total_rows < 0 || n_seg < 0) return 0;
+  return (int32_t)h3::vsa_num_blocks_bound(total_rows, n_seg);
+}
+
+size_t h3_vsa_workspace_bytes(int32_t total_rows, int32_t n_seg, int32_t H) {
+  if (total_rows < 0 || n_seg < 0 || H <= 0) return 0;
+  return h3::vsa_workspace_bytes(total_rows, n_seg, H);
+}
+
+namespace {
+// Key blocks of one segment that the selection keeps in LDS (64 KB of scores).
+constexpr int32_t kVsaMaxSegmentBlocks = 16384;
+
+h3_status vsa_common_checks(int32_t n_seg, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, float scale,
+                            int32_t topk) {
+  h3_status st = check_dims(H, D, dt);
+  if (st != H3_OK) return st;
+  if (D != 128) return H3_ERR_UNSUPPORTED;
+  if (n_seg < 0 || total_rows < 0 || total_rows > kMaxRows || topk < 1) return H3_ERR_SHAPE;
+  if (!(scale >= 0.f) || !isfinite(scale)) return H3_ERR_UNSUPPORTED;
+  return H3_OK;
+}
+}  // namespace
+
+h3_status h3_vsa_select(const void* q, const void* k, const int32_t* cu_seqlens, int32_t n_seg,
+                        int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                        float softmax_scale, int32_t topk, int32_t* sel, float* qmean, float* kmean,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  h3_status st = vsa_common_checks(n_seg, total_rows, H, D, dt, softmax_scale, topk);
+  if (st != H3_OK) return st;
+  if (max_seqlen < 0) return H3_ERR_SHAPE;
+  if ((max_seqlen + 63) / 64 > kVsaMaxSegmentBlocks) return H3_ERR_UNSUPPORTED;
+  if (total_rows == 0 || n_seg == 0) return H3_OK;
+  if (!q || !k || !cu_seqlens || !sel) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || (qmean && !aligned16(qmean)) || (kmean && !aligned16(kmean)))
+    return H3_ERR_ALIGN;
+  if (!workspace || workspace_bytes < h3::vsa_workspace_bytes(total_rows, n_seg, H)) return H3_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)D));
+  return from_hip(h3::launch_vsa_select(q, k, cu_seqlens, n_seg, max_seqlen, total_rows, H, dt == H3_BF16, topk,
+                                        scale, sel, qmean, kmean, workspace, stream));
+}
+
+h3_status h3_vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_seg,
+                          int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, float softmax_scale,
+                          const int32_t* sel, int32_t topk, void* o, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  h3_status st = vsa_common_checks(n_seg, total_rows, H, D, dt, softmax_scale, topk);
+  if (st != H3_OK) return st;
+  if (dt != H3_BF16) return H3_ERR_UNSUPPORTED;
+  if (total_rows == 0 || n_seg == 0) return H3_OK;
+  if (!q || !k || !v || !cu_seqlens || !sel || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!workspace || workspace_bytes < h3::vsa_workspace_bytes(total_rows, n_seg, H)) return H3_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)D));
+  return from_hip(h3::launch_vsa_attn(q, k, v, o, cu_seqlens, n_seg, total_rows, H, topk, scale, sel, workspace,
+                                      stream));
+}
+
 h3_status h3_validate_seqlens(const int32_t* cu_seqlens, int32_t n_seg, int32_t capacity,
                               hipStream_t stream) {
   if (n_seg < 0 || capacity < 0) return H3_ERR_SHAPE;

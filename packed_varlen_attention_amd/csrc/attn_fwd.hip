@@ -23,13 +23,10 @@
 // head dim 64): 128-row tiles, 32 rows per wave, two workgroups per CU, K rows
 // read in a permuted order so each lane's S^T registers hold 8 consecutive keys
 // (the B-operand layout), V transposed into LDS by the loading threads.
-#include "h3_internal.h"
+#include "attn_common.h"
 
 namespace h3 {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kBN = 64;      // keys per K/V tile
@@ -41,15 +38,6 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int k_row_perm(int m) {
   const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
   return ((a >> 1) << 4) | (g << 3) | ((a & 1) << 2) | b;
-}
-
-__device__ __forceinline__ int find_segment(const int32_t* __restrict__ prefix, int n_seg, int t) {
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 template <int D>
@@ -281,35 +269,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 //     rare rescale.  Row sums use v_dot2c_f32_bf16 over the bf16 P that the
 //     PV product actually uses.
 // ---------------------------------------------------------------------------
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 constexpr int kBM2 = 256;                 // query rows per workgroup
-constexpr int kTileBytes = 64 * 128 * 2;  // one 64-key K or V tile
 constexpr int kStages = 4;                // ring stages (tiles requested kStages-2 ahead)
-constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
-// Buffer descriptor word 3 for raw (unformatted, unswizzled) dword access.
-constexpr int kBufferWord3 = 0x00020000;
-
-// K tile: chunk c of row r sits at slot c ^ (r & 15); conflict-free for the
-// 32-row b128 reads of the S^T A operand.
-__device__ __forceinline__ int swz_k(int row) { return row & 15; }
-// V tile: slot c ^ {0, 6, 10, 12}[r & 3]; conflict-free for the transpose reads.
-__device__ __forceinline__ int swz_v(int row) { return (0xCA60 >> ((row & 3) << 2)) & 15; }
-
-__device__ __forceinline__ float swap_halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-template <int N>
-struct Int { static constexpr int value = N; };
 
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,

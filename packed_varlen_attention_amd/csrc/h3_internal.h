@@ -51,6 +51,18 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
 hipError_t launch_build_tiles(const int32_t* cu, int n_seg, int total_rows, int bm,
                               int32_t* tile_prefix, hipStream_t stream);
 
+// ---- VSA block-sparse attention (vsa.hip) ----------------------------------
+// Blocks are 64 consecutive rows of a segment; vsa_num_blocks_bound bounds
+// their count (the row count of the selection array).
+int64_t vsa_num_blocks_bound(int64_t total_rows, int64_t n_seg);
+size_t vsa_workspace_bytes(int64_t total_rows, int64_t n_seg, int64_t H);
+hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, int n_seg, int max_seqlen,
+                             int total_rows, int H, bool bf16, int topk, float scale, int32_t* sel,
+                             float* qmean_out, float* kmean_out, void* ws, hipStream_t stream);
+hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, void* o, const int32_t* cu, int n_seg,
+                           int total_rows, int H, int topk, float scale, const int32_t* sel, void* ws,
+                           hipStream_t stream);
+
 // ---- unpack (unpack.hip) ---------------------------------------------------
 size_t unpack_workspace_bytes(int64_t n);
 struct UnpackOut {

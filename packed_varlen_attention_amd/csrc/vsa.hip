@@ -1,0 +1,552 @@
+// VSA-style block-sparse varlen attention for gfx950, head dim 128.
+//
+// [P3] "突破视频生成大模型的工程瓶颈", sparse-attention section (VSA, block-level
+// sparse attention): the video tensor is cut into 4 x 4 x 4 = 64-token
+// blocks; a gate scores every block's relevance to the current query; only
+// the top-k blocks take part; standard attention runs among the kept blocks.
+// The pages give neither the gate nor the top-k share.  Here:
+//   * a block is 64 consecutive packed rows of one segment (the caller lays
+//     the video grid out cube by cube); a segment's last block may be short;
+//   * the gate is the scaled dot product of block means,
+//     score(b, c) = mean(Q_b) . mean(K_c) * scale, per head;
+//   * every (head, query block) keeps the top-k key blocks of its segment,
+//     larger score first, equal scores by lower block index.
+//
+// Three kernels:
+//   1. vsa_pool_kernel: fp32 means of the Q and K rows of every block
+//      (one pass over Q and K, HBM-bound);
+//   2. vsa_select_kernel: one workgroup per (head, query block) scores all
+//      key blocks of the segment into LDS (one lane per key block, the query
+//      mean broadcast from LDS) and picks the top-k with a 4-pass 8-bit radix
+//      select on order-preserving keys, then an ordered compaction, so the
+//      list comes out in increasing block order;
+//   3. vsa_attn_kernel: one workgroup of 2 waves per (head, query block),
+//      32 query rows per wave; every kept block's K and V (64 keys x 256 B)
+//      goes HBM -> LDS by direct loads into one 32 KB stage, and the tile is
+//      consumed with the dense kernel's operand layout (Q pre-scaled by
+//      scale * log2 e in registers, S^T = K Q^T on 32x32x16 bf16 MFMA with
+//      -m folded into the accumulator input, transposed V reads, bf16 P).
+//      Four workgroups share a CU (LDS 32 KB, 256 VGPRs each), so one
+//      workgroup's loads overlap the others' MFMAs.
+#include "attn_common.h"
+
+namespace h3 {
+namespace {
+
+constexpr int kVsaBlock = 64;
+constexpr int kPoolThreads = 256;
+constexpr int kSelThreads = 256;
+
+// ---------------------------------------------------------------------------
+// 1. block means.  Grid: nb_cap workgroups (an upper bound of the block
+// count); workgroup j handles block j if j < bprefix[n_seg].
+// qmean, kmean: fp32 [nb_cap][H][D].
+// ---------------------------------------------------------------------------
+template <bool kBF16>
+__global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ bprefix, int n_seg, int total_rows, int H, int D,
+    float* __restrict__ qmean, float* __restrict__ kmean) {
+  const int j = blockIdx.x;
+  if (j >= bprefix[n_seg]) return;
+  const int s = find_segment(bprefix, n_seg, j);
+  const int seg_start = min(max(cu[s], 0), total_rows);
+  const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+  const int r0 = seg_start + (j - bprefix[s]) * kVsaBlock;
+  const int r1 = min(r0 + kVsaBlock, seg_end);
+  const float inv = 1.f / (float)(r1 - r0);
+  const int64_t rs = (int64_t)H * D;
+  const int nch = (int)(rs >> 3);   // 8-element chunks per row
+  float4* qm = reinterpret_cast<float4*>(qmean + (int64_t)j * rs);
+  float4* km = reinterpret_cast<float4*>(kmean + (int64_t)j * rs);
+  for (int c = threadIdx.x; c < nch; c += kPoolThreads) {
+    float aq[8], ak[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aq[e] = ak[e] = 0.f;
+    for (int r = r0; r < r1; ++r) {
+      if constexpr (kBF16) {
+        const uint4 xq = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + r * rs)[c];
+        const uint4 xk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + r * rs)[c];
+        const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w}, wk[4] = {xk.x, xk.y, xk.z, xk.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aq[2 * e] += __uint_as_float(wq[e] << 16);
+          aq[2 * e + 1] += __uint_as_float(wq[e] & 0xffff0000u);
+          ak[2 * e] += __uint_as_float(wk[e] << 16);
+          ak[2 * e + 1] += __uint_as_float(wk[e] & 0xffff0000u);
+        }
+      } else {
+        const float4* pq = reinterpret_cast<const float4*>(static_cast<const float*>(q) + r * rs);
+        const float4* pk = reinterpret_cast<const float4*>(static_cast<const float*>(k) + r * rs);
+        const float4 q0 = pq[2 * c], q1 = pq[2 * c + 1], k0 = pk[2 * c], k1 = pk[2 * c + 1];
+        aq[0] += q0.x; aq[1] += q0.y; aq[2] += q0.z; aq[3] += q0.w;
+        aq[4] += q1.x; aq[5] += q1.y; aq[6] += q1.z; aq[7] += q1.w;
+        ak[0] += k0.x; ak[1] += k0.y; ak[2] += k0.z; ak[3] += k0.w;
+        ak[4] += k1.x; ak[5] += k1.y; ak[6] += k1.z; ak[7] += k1.w;
+      }
+    }
+    qm[2 * c] = make_float4(aq[0] * inv, aq[1] * inv, aq[2] * inv, aq[3] * inv);
+    qm[2 * c + 1] = make_float4(aq[4] * inv, aq[5] * inv, aq[6] * inv, aq[7] * inv);
+    km[2 * c] = make_float4(ak[0] * inv, ak[1] * inv, ak[2] * inv, ak[3] * inv);
+    km[2 * c + 1] = make_float4(ak[4] * inv, ak[5] * inv, ak[6] * inv, ak[7] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. scores and top-k.  Grid: H * nb_cap workgroups, (h, b) = (w / nb_cap,
+// w % nb_cap), exiting when b >= bprefix[n_seg].  Segments with more than
+// max_blocks key blocks (the host bound from max_seqlen) score only their
+// first max_blocks blocks.
+// sel: int32 [H][nb_cap][topk], global block numbers in increasing order,
+// -1 past the segment's block count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive scan of one int per thread (kSelThreads threads);
+// returns the prefix and writes the total to *total.  Uses `buf`
+// (kSelThreads ints of LDS); ends with a barrier.
+__device__ int block_excl_scan(int x, int* buf, int* total) {
+  const int tid = threadIdx.x;
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const int y = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += y;
+    __syncthreads();
+  }
+  const int incl = buf[tid];
+  *total = buf[kSelThreads - 1];
+  __syncthreads();
+  return incl - x;
+}
+
+__global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
+    const float* __restrict__ qmean, const float* __restrict__ kmean, const int32_t* __restrict__ bprefix,
+    int n_seg, int H, int nb_cap, int max_blocks, int topk, float scale, int32_t* __restrict__ sel) {
+  constexpr int D = 128;
+  extern __shared__ float lds_f[];   // scores [max_blocks] then keys as uint32 (aliased)
+  __shared__ float s_q[D];
+  __shared__ int s_hist[256];
+  __shared__ int s_scan[kSelThreads];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+
+  const int64_t w = blockIdx.x;
+  const int h = (int)(w / nb_cap), b = (int)(w - (int64_t)h * nb_cap);
+  const int nb = bprefix[n_seg];
+  if (h >= H || b >= nb) return;
+  const int s = find_segment(bprefix, n_seg, b);
+  const int cb0 = bprefix[s];
+  const int n_kb = min(bprefix[s + 1] - cb0, max_blocks);
+  const int tid = threadIdx.x;
+  int32_t* out = sel + ((int64_t)h * nb_cap + b) * topk;
+
+  if (tid < D) s_q[tid] = qmean[((int64_t)b * H + h) * D + tid] * scale;
+  __syncthreads();
+
+  // scores: one thread per key block, the query mean broadcast from LDS
+  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
+  for (int c = tid; c < n_kb; c += kSelThreads) {
+    const float4* km = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c) * H + h) * D);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 x = km[d4];
+      acc = fmaf(x.x, s_q[4 * d4], acc);
+      acc = fmaf(x.y, s_q[4 * d4 + 1], acc);
+      acc = fmaf(x.z, s_q[4 * d4 + 2], acc);
+      acc = fmaf(x.w, s_q[4 * d4 + 3], acc);
+    }
+    keys[c] = order_key(acc);
+  }
+  if (tid == 0) { s_prefix = 0u; s_need = min(topk, n_kb); }
+  __syncthreads();
+
+  const int need_total = min(topk, n_kb);
+  uint32_t thresh = 0u;     // keys >= thresh are candidates; > thresh all kept
+  int need_eq = 0;          // how many keys equal to thresh are kept (lowest index first)
+  if (n_kb > topk) {
+    // radix select of the topk-th largest key, 8 bits per pass from the top
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0;
+      __syncthreads();
+      const uint32_t pre = s_prefix;
+      for (int c = tid; c < n_kb; c += kSelThreads) {
+        const uint32_t key = keys[c];
+        if ((key & hi_mask) == pre) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      // wave 0: lane l owns digits 255-4l .. 252-4l (descending); find the
+      // digit where the count of larger-or-equal keys reaches s_need
+      if (tid < 64) {
+        const int lane = tid;
+        int cnt[4];
+        int sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { cnt[e] = s_hist[255 - 4 * lane - e]; sum += cnt[e]; }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        const int excl = incl - sum;
+        const int need = s_need;
+        if (excl < need && incl >= need) {
+          int run = excl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (run + cnt[e] >= need) {
+              const uint32_t digit = (uint32_t)(255 - 4 * lane - e);
+              s_prefix = pre | (digit << shift);
+              s_need = need - run;
+              break;
+            }
+            run += cnt[e];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    thresh = s_prefix;
+    need_eq = s_need;
+  }
+
+  // ordered compaction over contiguous per-thread chunks: keys > thresh all
+  // kept, keys == thresh kept for the first need_eq of them in index order
+  const int chunk = (n_kb + kSelThreads - 1) / kSelThreads;
+  const int c_lo = min(tid * chunk, n_kb), c_hi = min(c_lo + chunk, n_kb);
+  int n_eq = 0;
+  if (n_kb > topk)
+    for (int c = c_lo; c < c_hi; ++c) n_eq += keys[c] == thresh;
+  int tot;
+  const int eq_before = block_excl_scan(n_eq, s_scan, &tot);
+  // count kept per thread (equal keys: by their rank among equal keys)
+  int n_keep = 0;
+  {
+    int eq_rank = eq_before;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const uint32_t key = keys[c];
+      bool keep;
+      if (n_kb <= topk) keep = true;
+      else if (key > thresh) keep = true;
+      else if (key == thresh) keep = eq_rank++ < need_eq;
+      else keep = false;
+      n_keep += keep;
+    }
+  }
+  const int keep_before = block_excl_scan(n_keep, s_scan, &tot);
+  {
+    int eq_rank = eq_before, pos = keep_before;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const uint32_t key = keys[c];
+      bool keep;
+      if (n_kb <= topk) keep = true;
+      else if (key > thresh) keep = true;
+      else if (key == thresh) keep = eq_rank++ < need_eq;
+      else keep = false;
+      if (keep && pos < topk) out[pos++] = cb0 + c;
+    }
+  }
+  for (int i = need_total + tid; i < topk; i += kSelThreads) out[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// 3. block-sparse attention.  Grid: 8 * ceil(H * nb_cap / 8) workgroups of
+// 128 threads, head-major and cut into 8 contiguous chunks (one per XCD) like
+// the dense kernel; item w = (h, b) = (w / nb_cap, w % nb_cap).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ bprefix,
+    const int32_t* __restrict__ sel, int n_seg, int H, int total_rows, int nb_cap, int topk,
+    float scale_log2) {
+  constexpr int D = 128;
+  constexpr int NW = 2;                    // waves per workgroup
+  constexpr int DMA_ROWS = 64 / NW;        // tile rows each wave loads per tensor
+  constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
+  __shared__ __attribute__((aligned(1024))) char lk[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lv[kTileBytes];
+
+  const int64_t W = (int64_t)H * nb_cap;
+  const int64_t per = (W + 7) >> 3;
+  const int64_t jj = blockIdx.x >> 3;
+  const int64_t w = (int64_t)(blockIdx.x & 7) * per + jj;
+  if (jj >= per || w >= W) return;
+  const int h = (int)(w / nb_cap), b = (int)(w - (int64_t)h * nb_cap);
+  if (b >= bprefix[n_seg]) return;
+  const int s = find_segment(bprefix, n_seg, b);
+  const int seg_start = min(max(cu[s], 0), total_rows);
+  const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+  const int cb0 = bprefix[s];
+  const int r0 = seg_start + (b - cb0) * kVsaBlock;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int64_t rs = (int64_t)H * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  // ---- direct HBM -> LDS loads of one 64-row block: wave w fills rows
+  // 32w .. 32w+31, four rows (1 KB) per instruction
+  // Byte offset (within the block) of the 16-byte chunk that the swizzle
+  // places in this lane's LDS slot for load tt, given the tile row it reads.
+  auto dma_off = [&](int tt, int row, bool is_v) __attribute__((always_inline)) {
+    const int trow = DMA_ROWS * wave + 4 * tt + (lane >> 4);
+    const int ch = (lane & 15) ^ (is_v ? swz_v(trow) : swz_k(trow));
+    return (uint32_t)row * row_bytes + (uint32_t)ch * 16u;
+  };
+  const uint16_t* kh = k + (int64_t)h * D;
+  const uint16_t* vh = v + (int64_t)h * D;
+  auto issue_block = [&](int kr0, int len) __attribute__((always_inline)) {
+    const int nrec = (int)(64u * row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
+#pragma unroll
+    for (int tt = 0; tt < DMA_INSTR; ++tt) {
+      // ragged block: rows past its end repeat its last row
+      const int row = min(DMA_ROWS * wave + 4 * tt + (lane >> 4), len - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                               dma_off(tt, row, false), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                               dma_off(tt, row, true), 0, 0, 0);
+    }
+  };
+
+  // ---- Q fragment (B operand) times scale * log2(e)
+  bf16x8_t qf[8];
+  const int qrow = r0 + wave * 32 + r32;
+  const int q_end = min(r0 + kVsaBlock, seg_end);
+  if (qrow < q_end) {
+    const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      qf[kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kc][e] = (__bf16)((float)qf[kc][e] * scale_log2);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) qf[kc] = bf16x8_t{};
+  }
+
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
+  int voff[4];
+  {
+    const int rl = 4 * g + ((lane & 15) >> 2);
+    const int sv = swz_v(rl);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
+  }
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+  float m_run = 0.f, l_run = 0.f;
+  f32x16_t neg_m = f32x16_t{};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto compute_s = [&](int half, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(lk + half * 8192 + koff[kc]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
+                                                     0, 0, 0);
+    }
+  };
+  auto mask_tail = [&](f32x16_t& sacc, int key_rel, int len) __attribute__((always_inline)) {
+    if (key_rel + 32 > len) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= len) sacc[i] = -INFINITY;
+      }
+    }
+  };
+  auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    return mx;
+  };
+  auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
+    float lsum = l_run;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+      }
+    }
+    l_run = lsum;
+  };
+  auto pv_half = [&](int half, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const char* vp = lv + half * 8192 + voff[db] + (16 * c) * 256;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
+      }
+  };
+
+  const int32_t* my_sel = sel + ((int64_t)h * nb_cap + b) * topk;
+  const int seg_blocks = bprefix[s + 1] - cb0;
+  bool first = true;
+  for (int t = 0; t < topk; ++t) {
+    const int c = my_sel[t];
+    if (c < 0) break;
+    const int cl = c - cb0;
+    if (cl < 0 || cl >= seg_blocks) continue;   // not a block of this segment: skipped
+    const int kr0 = seg_start + cl * kVsaBlock;
+    const int len = min(kVsaBlock, seg_end - kr0);
+    issue_block(kr0, len);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the block landed
+    __syncthreads();
+    // two 32-key halves, each: S, reference / rescale test, P, O += V P
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x16_t sacc;
+      compute_s(half, sacc, !first);
+      mask_tail(sacc, 32 * half, len);
+      const float mloc = lane_max(sacc);
+      if (first) {
+        // the first half of the first kept block sets the reference
+        m_run = swap_halves_max(mloc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] -= m_run;
+          neg_m[i] = -m_run;
+        }
+        first = false;
+      } else if (__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0) {
+        // rare: scores exceed the reference by more than 2^8
+        const float mpair = swap_halves_max(mloc);
+        const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        m_run += delta;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] -= delta;
+          neg_m[i] = -m_run;
+        }
+      }
+      bf16x8_t pk[2];
+      exp_half(sacc, pk);
+      pv_half(half, pk);
+    }
+    __syncthreads();                      // the stage is free for the next block
+  }
+
+  if (qrow < q_end && !first) {
+    const float inv = 1.f / swap_halves_sum(l_run);
+    uint16_t* op = o + qrow * rs + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 st;
+        const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
+        const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
+        const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
+        const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
+        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
+      }
+  }
+}
+
+}  // namespace
+
+int64_t vsa_num_blocks_bound(int64_t total_rows, int64_t n_seg) {
+  return ceil_div(total_rows, kVsaBlock) + n_seg;
+}
+
+size_t vsa_workspace_bytes(int64_t total_rows, int64_t n_seg, int64_t H) {
+  const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  return align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256) +
+         2 * align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
+}
+
+namespace {
+struct VsaWs {
+  int32_t* bprefix;
+  float* qmean;
+  float* kmean;
+};
+VsaWs carve(void* ws, int64_t total_rows, int64_t n_seg, int64_t H) {
+  const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  char* w = static_cast<char*>(ws);
+  VsaWs r;
+  r.bprefix = reinterpret_cast<int32_t*>(w);
+  w += align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256);
+  r.qmean = reinterpret_cast<float*>(w);
+  w += align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
+  r.kmean = reinterpret_cast<float*>(w);
+  return r;
+}
+}  // namespace
+
+hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, int n_seg, int max_seqlen,
+                             int total_rows, int H, bool bf16, int topk, float scale, int32_t* sel,
+                             float* qmean_out, float* kmean_out, void* ws, hipStream_t stream) {
+  const VsaWs w = carve(ws, total_rows, n_seg, H);
+  // block prefix (the dense kernel's tile-count scan with 64-row tiles)
+  hipError_t e = launch_build_tiles(cu, n_seg, total_rows, kVsaBlock, w.bprefix, stream);
+  if (e != hipSuccess) return e;
+  const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  float* qm = qmean_out ? qmean_out : w.qmean;
+  float* km = kmean_out ? kmean_out : w.kmean;
+  if (bf16)
+    vsa_pool_kernel<true><<<(unsigned)nb_cap, kPoolThreads, 0, stream>>>(q, k, cu, w.bprefix, n_seg, total_rows,
+                                                                         H, 128, qm, km);
+  else
+    vsa_pool_kernel<false><<<(unsigned)nb_cap, kPoolThreads, 0, stream>>>(q, k, cu, w.bprefix, n_seg, total_rows,
+                                                                          H, 128, qm, km);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int max_blocks = (int)std::min<int64_t>(ceil_div(std::max(max_seqlen, 1), kVsaBlock), nb_cap);
+  const size_t lds = (size_t)max_blocks * 4;
+  vsa_select_kernel<<<(unsigned)(nb_cap * H), kSelThreads, lds, stream>>>(qm, km, w.bprefix, n_seg, H, (int)nb_cap,
+                                                                         max_blocks, topk, scale, sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, void* o, const int32_t* cu, int n_seg,
+                           int total_rows, int H, int topk, float scale, const int32_t* sel, void* ws,
+                           hipStream_t stream) {
+  const VsaWs w = carve(ws, total_rows, n_seg, H);
+  hipError_t e = launch_build_tiles(cu, n_seg, total_rows, kVsaBlock, w.bprefix, stream);
+  if (e != hipSuccess) return e;
+  const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  const int64_t grid = 8 * ceil_div(nb_cap * H, 8);
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  vsa_attn_kernel<<<(unsigned)grid, 128, 0, stream>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(o), cu, w.bprefix, sel, n_seg, H, total_rows, (int)nb_cap, topk, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
@@ -179,3 +179,27 @@ def test_sigma_schedule_host_matches_oracle(lib):
     assert lib.h3_sigma_schedule(0, 3.0, out) == SHAPE
     assert lib.h3_sigma_schedule(1, 0.0, out) == UNSUPPORTED
     assert lib.h3_sigma_schedule(1, 3.0, None) == NULL
+
+
+def test_vsa_host_validation(lib):
+    sel = P
+    sel_f = lib.h3_vsa_select
+    a = lib.h3_vsa_attn_fwd
+    ok = dict(n_seg=2, rows=300, H=4, D=128, dt=0, scale=0.0, topk=4)
+    def S(q=P, k=P, cu=P, n_seg=2, max_seqlen=256, rows=300, H=4, D=128, dt=0, scale=0.0, topk=4, sel=P,
+          ws=P, wsb=1 << 30):
+        return sel_f(q, k, cu, n_seg, max_seqlen, rows, H, D, dt, scale, topk, sel, None, None, ws, wsb, None)
+    def A(q=P, cu=P, n_seg=2, rows=300, H=4, D=128, dt=0, scale=0.0, sel=P, topk=4, o=P, ws=P, wsb=1 << 30):
+        return a(q, P, P, cu, n_seg, rows, H, D, dt, scale, sel, topk, o, ws, wsb, None)
+    assert S(D=64) == UNSUPPORTED and A(D=64) == UNSUPPORTED
+    assert S(topk=0) == SHAPE and A(topk=0) == SHAPE
+    assert S(max_seqlen=-1) == SHAPE
+    assert S(max_seqlen=(1 << 20) + 64) == UNSUPPORTED
+    assert A(dt=1) == UNSUPPORTED                    # the sparse kernel is bf16 only
+    assert S(scale=-1.0) == UNSUPPORTED
+    assert S(q=None) == NULL and A(sel=None) == NULL
+    assert S(q=MIS) == ALIGN and A(o=MIS) == ALIGN
+    assert S(wsb=1) == WORKSPACE and A(ws=None) == WORKSPACE
+    assert S(rows=0, q=None, k=None) == OK and A(n_seg=0, q=None, o=None) == OK
+    assert lib.h3_vsa_blocks_bound(300, 2) == 5 + 2
+    assert lib.h3_vsa_workspace_bytes(300, 2, 4) >= 2 * 7 * 4 * 128 * 4

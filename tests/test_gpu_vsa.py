@@ -1,0 +1,152 @@
+"""GPU parity of VSA-style block-sparse attention (h3_vsa_select and
+h3_vsa_attn_fwd through the C ABI) against the CPU oracle.
+
+The selection is an integer result decided by floating-point scores: block
+means are compared at fp32 tolerance, the GPU's selection must be a valid
+top-k of the oracle's fp64 scores (every kept block scores at least as high
+as every dropped one, up to a rounding margin far below the score spread) and
+equal to the oracle's selection wherever the k-th and (k+1)-th scores are
+separated by more than that margin; exact ties are broken by lower block
+number on both sides.  Attention is checked stage-wise (the oracle's sparse
+attention on the GPU's own selection) at the bf16 tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_varlen_attention_amd as h3
+import workloads as W
+from gpu_common import F32_MAX_ABS, assert_close, errors, f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MARGIN = 1e-6      # fp32 rounding of a 128-term dot product of block means, with room
+
+
+def _packed(lengths, H, seed, dup=None):
+    """Packed bf16 Q, K, V [rows, H, 128] for segments of `lengths` (RoPE
+    plays no part in the block-sparse path, so the rows are drawn packed)."""
+    rows = int(sum(lengths))
+    cap = max(64, (rows + 63) // 64 * 64)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    t = [(torch.randn((cap, H, 128), generator=g) * 0.5).to(torch.bfloat16) for _ in range(3)]
+    if dup is not None:                      # copy key block dup[0] over dup[1] (exact score ties)
+        a, b = dup
+        t[1][b * 64:(b + 1) * 64] = t[1][a * 64:(a + 1) * 64]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return t, cu, rows
+
+
+def _check_selection(sel_gpu, q, k, cu, topk):
+    sel_o = oracle.vsa_select(q, k, cu, topk)
+    scores = oracle.vsa_scores(q, k, cu)
+    _, _, bcu = oracle.block_layout(cu)
+    H = q.shape[1]
+    n_exact = 0
+    for s, S in enumerate(scores):
+        a = int(bcu[s])
+        n_s = S.shape[1]
+        for h in range(H):
+            for bl in range(n_s):
+                got = sel_gpu[h, a + bl]
+                kept = [int(c) for c in got if c >= 0]
+                assert kept == sorted(set(kept)) and len(kept) == min(topk, n_s)
+                assert all(a <= c < a + n_s for c in kept)
+                assert (got[len(kept):] == -1).all()
+                row = S[h, bl]
+                loc = [c - a for c in kept]
+                drop = [c for c in range(n_s) if c not in loc]
+                if drop:
+                    assert row[loc].min() >= row[drop].max() - MARGIN
+                srt = np.sort(row)[::-1]
+                if n_s <= topk or srt[topk - 1] - srt[topk] > MARGIN:
+                    assert got.tolist() == sel_o[h, a + bl].tolist()
+                    n_exact += 1
+    return n_exact
+
+
+@pytest.mark.parametrize("topk", [1, 3, 8])
+def test_vsa_ragged_segments_means_selection_attention(topk):
+    lengths = [1, 63, 64, 65, 0, 200, 129, 700]
+    H = 3
+    (q, k, v), cu, rows = _packed(lengths, H, seed=11)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    sel, qm, km = h3.vsa_select(dq, dk, dcu, rows, topk, max_seqlen=max(lengths), means=True)
+    o = torch.full_like(dq, float("nan"))
+    h3.vsa_attn_fwd(dq, dk, dv, dcu, rows, sel, topk, o=o)
+    torch.cuda.synchronize()
+    q64, k64, v64 = W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows])
+    nb = oracle.block_layout(cu)[2][-1]
+    for got, x in ((qm, q64), (km, k64)):
+        max_abs, _ = errors(got[:nb], oracle.block_means(x, cu))
+        assert max_abs <= F32_MAX_ABS
+    sel_np = sel[:, :nb].cpu().numpy()
+    n_exact = _check_selection(sel_np, q64, k64, cu, topk)
+    assert n_exact > 0
+    ref = oracle.vsa_attention(q64, k64, v64, cu, sel_np)
+    assert_close(o[:rows], ref, "bf16", "VSA O stage-wise")
+    assert torch.isnan(o[rows:].float()).all()          # rows past total_rows untouched
+
+
+def test_vsa_exact_ties_break_to_lower_block():
+    (q, k, v), cu, rows = _packed([64 * 6], 2, seed=12, dup=(1, 4))
+    dcu = torch.from_numpy(cu).cuda()
+    sel = h3.vsa_select(q.cuda(), k.cuda(), dcu, rows, 2, max_seqlen=rows)
+    torch.cuda.synchronize()
+    got = sel[:, :6].cpu().numpy()
+    want = oracle.vsa_select(W.to_f64(q[:rows]), W.to_f64(k[:rows]), cu, 2)
+    assert np.array_equal(got, want)
+    for h in range(2):
+        for b in range(6):
+            assert not (4 in got[h, b] and 1 not in got[h, b])
+
+
+def test_vsa_keep_every_block_equals_dense_attention():
+    lengths = [300, 64, 5]
+    (q, k, v), cu, rows = _packed(lengths, 2, seed=13)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    sel = h3.vsa_select(dq, dk, dcu, rows, 16, max_seqlen=300)
+    o = h3.vsa_attn_fwd(dq, dk, dv, dcu, rows, sel, 16)
+    torch.cuda.synchronize()
+    ref = oracle.attention(W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows]), cu)
+    assert_close(o[:rows], ref, "bf16", "VSA keep-all vs dense oracle")
+
+
+def test_vsa_full_size_cube_grid_sampled():
+    # the measured configuration: 59,904 cube-ordered video tokens, 40 heads,
+    # 936 blocks, top-117 (one block in eight)
+    wl = W.make_vsa_workload()
+    q, k, v = W.make_qkv_on_device(wl, "cuda", seed=5)
+    cu = torch.tensor([0, wl.n], dtype=torch.int32, device="cuda")
+    topk = 117
+    sel = h3.vsa_select(q, k, cu, wl.n, topk, max_seqlen=wl.n)
+    o = h3.vsa_attn_fwd(q, k, v, cu, wl.n, sel, topk)
+    torch.cuda.synchronize()
+    heads = [0, 21, 39]
+    qs, ks, vs = f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads])
+    sel_np = sel[heads].cpu().numpy()
+    cu_np = np.array([0, wl.n])
+    # the selection of sampled query blocks against fp64 scores
+    qm, km = oracle.block_means(qs, cu_np), oracle.block_means(ks, cu_np)
+    rng = np.random.default_rng(1)
+    blocks = np.unique(np.concatenate([[0, 935], rng.integers(0, 936, 10)]))
+    sc = 1 / np.sqrt(128)
+    for hi in range(3):
+        for b in blocks:
+            row = km[:, hi] @ qm[b, hi] * sc
+            kept = sel_np[hi, b]
+            assert len(set(kept.tolist())) == topk and (kept >= 0).all()
+            drop = np.setdiff1d(np.arange(936), kept)
+            assert row[kept].min() >= row[drop].max() - MARGIN
+            # attention of the block's rows over the kept keys
+            keys = np.concatenate([np.arange(64 * c, 64 * c + 64) for c in kept])
+            S = qs[64 * b:64 * b + 64, hi] @ ks[keys, hi].T * sc
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            ref = (P / P.sum(axis=1, keepdims=True)) @ vs[keys, hi]
+            got = f64(o[64 * b:64 * b + 64, heads[hi]])
+            assert np.abs(got - ref).max() <= 2e-2
+            assert np.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 5e-3

@@ -347,3 +347,37 @@ def make_continuation_small(H: int = 4, D: int = 128, T_ref: int = 3, T_tgt: int
     return Workload(name="continuation_small_%dtok" % n, index=103, n=n, n_seg=1, H=H, D=D,
                     dtype="bf16", capacity=_round_up(n, ALIGN), time_offset=238.0, q_scale=0.5,
                     tags=tags, pos=pos, seg=segv, rope=default_rope(D), groups=b.groups)
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse (VSA) layout: a video latent grid listed cube by cube, so that
+# every 64 consecutive tokens form one 4 x 4 x 4 block ("突破视频生成大模型的
+# 工程瓶颈", sparse-attention section: VSA cuts the video tensor into 4 x 4 x 4
+# = 64-token blocks).  Positions keep the grid coordinates, so RoPE is the same
+# as for the row-major layout.
+# ---------------------------------------------------------------------------
+def cube_order_video(T: int, Hh: int, W: int, cube: int = 4) -> np.ndarray:
+    """int32 [T*Hh*W, 3] (t, h, w) positions, cube-major: cubes row-major
+    over (t, h, w), tokens row-major inside a cube.  Dims must be multiples
+    of `cube`."""
+    assert T % cube == 0 and Hh % cube == 0 and W % cube == 0
+    ct, ch, cw, it, ih, iw = np.meshgrid(np.arange(T // cube), np.arange(Hh // cube), np.arange(W // cube),
+                                         np.arange(cube), np.arange(cube), np.arange(cube), indexing="ij")
+    t = (ct * cube + it).ravel()
+    h = (ch * cube + ih).ravel()
+    w = (cw * cube + iw).ravel()
+    return np.stack([t, h, w], axis=1).astype(np.int32)
+
+
+def make_vsa_workload(T: int = 24, Hh: int = 48, W: int = 52, H: int = 40, D: int = 128,
+                      index: int = 200) -> Workload:
+    """One segment of video tokens in cube order (T x Hh x W grid; the default
+    24 x 48 x 52 = 59,904 tokens is the 58,758-token step's video grid rounded
+    up to whole 4 x 4 x 4 cubes: 936 blocks)."""
+    p = cube_order_video(T, Hh, W)
+    n = p.shape[0]
+    tags = np.full(n, VIDEO, np.uint8)
+    seg = np.zeros(n, np.int32)
+    return Workload(name="vsa_video_%dx%dx%d_%dtok" % (T, Hh, W, n), index=index, n=n, n_seg=1, H=H, D=D,
+                    dtype="bf16", capacity=_round_up(n, ALIGN), time_offset=0.0, q_scale=0.5,
+                    tags=tags, pos=p, seg=seg, rope=default_rope(D), groups=[("video_cubes", VIDEO, n)])
