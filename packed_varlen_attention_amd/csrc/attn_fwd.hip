@@ -582,11 +582,24 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
     }
   }
 
-  // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3]
+  // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3].
+  // Each wave's 32 x 128 bf16 tile goes through LDS so that the global stores
+  // write whole rows (16 bytes per lane, 4 rows per instruction) instead of
+  // 16-byte pieces of 32 rows; on short segments, where the store sits on the
+  // critical path of every workgroup, this is ~10 % of the kernel.  Free LDS:
+  // every ring stage other than those of the last two tiles (all waves have
+  // passed the barrier after which nothing reads them, and every issued tile
+  // load has been waited for).
   const float inv = 1.f / swap_halves_sum(l_run);
-  const int qrow = q0 + wave * 32 + r32;
-  if (qrow < seg_end) {
-    uint16_t* op = o + qrow * rs + (int64_t)h * D;
+  {
+    const int busy0 = (ntiles - 1) & 3, busy1 = ntiles >= 2 ? (ntiles - 2) & 3 : busy0;
+    int f0 = 0;
+    while (f0 == busy0 || f0 == busy1) ++f0;
+    int f1 = f0 + 1;
+    while (f1 == busy0 || f1 == busy1) ++f1;
+    const int fs = (wave >> 2) ? f1 : f0;
+    char* base_l = ((wave >> 1) & 1) ? v_stage(fs) : k_stage(fs);
+    char* ot = base_l + (wave & 1) * 8192;      // 32 rows x 256 B, 16-byte chunks swizzled by row
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -598,8 +611,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
         const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
         st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
+        const int chunk = (4 * db + a4) ^ (r32 & 15);
+        *reinterpret_cast<uint2*>(ot + r32 * 256 + chunk * 16 + g * 8) = st;
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's tile is in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4), c = lane & 15;
+      const uint4 x = *reinterpret_cast<const uint4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+      const int orow = q0 + wave * 32 + row;
+      if (orow < seg_end) *reinterpret_cast<uint4*>(o + orow * rs + (int64_t)h * D + c * 8) = x;
+    }
   }
 }
 
