@@ -517,6 +517,7 @@ hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, in
   hipError_t e = launch_build_tiles(cu, n_seg, total_rows, kVsaBlock, w.bprefix, stream);
   if (e != hipSuccess) return e;
   const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  if (nb_cap * H > 0x7fffffff) return hipErrorInvalidValue;   // one workgroup per (head, block)
   float* qm = qmean_out ? qmean_out : w.qmean;
   float* km = kmean_out ? kmean_out : w.kmean;
   if (bf16)
@@ -542,6 +543,7 @@ hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, void* o,
   if (e != hipSuccess) return e;
   const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
   const int64_t grid = 8 * ceil_div(nb_cap * H, 8);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   vsa_attn_kernel<<<(unsigned)grid, 128, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
