@@ -46,6 +46,12 @@ const char* h3_status_string(h3_status s) {
   return "unknown status";
 }
 
+h3_status h3_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, hipStream_t stream) {
+  if (!out) return H3_ERR_NULL;
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20)) return H3_ERR_SHAPE;
+  return from_hip(h3::launch_mfma_probe(workgroups, iters, out, stream));
+}
+
 const char* h3_version(void) { return "h3 0.1.0 gfx950"; }
 
 size_t h3_pack_workspace_bytes(int32_t n, int32_t n_seg) {

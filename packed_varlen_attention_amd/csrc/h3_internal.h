@@ -84,4 +84,7 @@ hipError_t launch_unpack_euler(const void* o, const int32_t* perm, const uint8_t
                                const uint8_t* pinned, int n, int H, int D, bool bf16,
                                const EulerOut& eo, void* ws, hipStream_t stream);
 
+// ---- diagnostic (probe.hip) ------------------------------------------------
+hipError_t launch_mfma_probe(int workgroups, int iters, float* out, hipStream_t stream);
+
 }  // namespace h3
