@@ -48,7 +48,10 @@ const char* h3_status_string(h3_status s) {
 
 h3_status h3_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, hipStream_t stream) {
   if (!out) return H3_ERR_NULL;
-  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20)) return H3_ERR_SHAPE;
+  // at most 2^28 workgroup-iterations (~2.8e14 FLOP, a fraction of a second)
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20) ||
+      (int64_t)workgroups * iters > ((int64_t)1 << 28))
+    return H3_ERR_SHAPE;
   return from_hip(h3::launch_mfma_probe(workgroups, iters, out, stream));
 }
 

@@ -211,3 +211,4 @@ def test_probe_host_validation(lib):
     assert lib.h3_probe_mfma_bf16(0, 10, 0x1000, None) == 3                  # H3_ERR_SHAPE
     assert lib.h3_probe_mfma_bf16(512, 0, 0x1000, None) == 3
     assert lib.h3_probe_mfma_bf16((1 << 20) + 1, 10, 0x1000, None) == 3
+    assert lib.h3_probe_mfma_bf16(1 << 10, (1 << 18) + 1, 0x1000, None) == 3   # > 2^28 workgroup-iterations
