@@ -225,6 +225,23 @@ def test_online_softmax_rescale_every_few_tiles(D, rate):
     assert_close(o, ref, "bf16", "O rescale rate %g D %d" % (rate, D))
 
 
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (128, "f32")])
+def test_maximum_head_count(D, dtype):
+    # H = 4096, the most the ABI accepts: a token row is H*D elements (1 MiB in
+    # bf16 at D = 128) and a 64-row tile 64 MiB, the reach that the kernels'
+    # 32-bit tile-relative offsets are sized for.  Ragged segments of 70 and
+    # 130 rows, NaN pad rows up to the capacity; the oracle checks the first,
+    # a middle and the last heads (heads are independent).
+    # Inputs come from the seeded device generator (the CPU one takes ~45 s
+    # at this size); only the checked heads are copied to the host.
+    wl = W.make_custom([70, 130], H=4096, D=D, dtype=dtype, q_scale=0.5 if dtype == "bf16" else 1.0, index=7)
+    q, k, v = W.make_qkv_on_device(wl, "cuda")
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    heads = [0, 1, 2047, 4094, 4095]
+    qh, kh, vh = (t[:, heads].cpu() for t in (q, k, v))
+    _check_full(wl, g, _oracle_full(wl, qh, kh, vh), heads=heads)
+
+
 def test_softmax_scale_argument():
     wl = W.make_custom([200, 77], H=2, D=64)
     q, k, v = _packed_inputs(wl)
