@@ -124,45 +124,15 @@ __device__ int block_excl_scan(int x, int* buf, int* total) {
   return incl - x;
 }
 
-__global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
-    const float* __restrict__ qmean, const float* __restrict__ kmean, const int32_t* __restrict__ bprefix,
-    int n_seg, int H, int nb_cap, int max_blocks, int topk, float scale, int32_t* __restrict__ sel) {
-  constexpr int D = 128;
-  extern __shared__ float lds_f[];   // scores [max_blocks] then keys as uint32 (aliased)
-  __shared__ float s_q[D];
-  __shared__ int s_hist[256];
-  __shared__ int s_scan[kSelThreads];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_need;
-
-  const int64_t w = blockIdx.x;
-  const int h = (int)(w / nb_cap), b = (int)(w - (int64_t)h * nb_cap);
-  const int nb = bprefix[n_seg];
-  if (h >= H || b >= nb) return;
-  const int s = find_segment(bprefix, n_seg, b);
-  const int cb0 = bprefix[s];
-  const int n_kb = min(bprefix[s + 1] - cb0, max_blocks);
+// Top-k of one query block's keys (order_key of its scores, one per key
+// block of its segment, in LDS): writes the kept global block numbers cb0 + c
+// in increasing order to out[0 .. min(topk, n_kb)) and -1 to the rest.  Keys
+// larger than the k-th largest are all kept; among keys equal to it, the
+// lowest block indices.  Called by all kSelThreads threads; ends with the
+// writes (callers that reuse the LDS afterwards put a barrier first).
+__device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int topk, int cb0, int32_t* out,
+                                            int* s_hist, int* s_scan, uint32_t& s_prefix, int& s_need) {
   const int tid = threadIdx.x;
-  int32_t* out = sel + ((int64_t)h * nb_cap + b) * topk;
-
-  if (tid < D) s_q[tid] = qmean[((int64_t)b * H + h) * D + tid] * scale;
-  __syncthreads();
-
-  // scores: one thread per key block, the query mean broadcast from LDS
-  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
-  for (int c = tid; c < n_kb; c += kSelThreads) {
-    const float4* km = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c) * H + h) * D);
-    float acc = 0.f;
-#pragma unroll 8
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 x = km[d4];
-      acc = fmaf(x.x, s_q[4 * d4], acc);
-      acc = fmaf(x.y, s_q[4 * d4 + 1], acc);
-      acc = fmaf(x.z, s_q[4 * d4 + 2], acc);
-      acc = fmaf(x.w, s_q[4 * d4 + 3], acc);
-    }
-    keys[c] = order_key(acc);
-  }
   if (tid == 0) { s_prefix = 0u; s_need = min(topk, n_kb); }
   __syncthreads();
 
@@ -255,6 +225,128 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
     }
   }
   for (int i = need_total + tid; i < topk; i += kSelThreads) out[i] = -1;
+}
+
+__global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
+    const float* __restrict__ qmean, const float* __restrict__ kmean, const int32_t* __restrict__ bprefix,
+    int n_seg, int H, int nb_cap, int max_blocks, int topk, float scale, int32_t* __restrict__ sel) {
+  constexpr int D = 128;
+  extern __shared__ float lds_f[];   // scores [max_blocks] then keys as uint32 (aliased)
+  __shared__ float s_q[D];
+  __shared__ int s_hist[256];
+  __shared__ int s_scan[kSelThreads];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+
+  const int64_t w = blockIdx.x;
+  const int h = (int)(w / nb_cap), b = (int)(w - (int64_t)h * nb_cap);
+  const int nb = bprefix[n_seg];
+  if (h >= H || b >= nb) return;
+  const int s = find_segment(bprefix, n_seg, b);
+  const int cb0 = bprefix[s];
+  const int n_kb = min(bprefix[s + 1] - cb0, max_blocks);
+  const int tid = threadIdx.x;
+  int32_t* out = sel + ((int64_t)h * nb_cap + b) * topk;
+
+  if (tid < D) s_q[tid] = qmean[((int64_t)b * H + h) * D + tid] * scale;
+  __syncthreads();
+
+  // scores: one thread per key block, the query mean broadcast from LDS
+  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
+  for (int c = tid; c < n_kb; c += kSelThreads) {
+    const float4* km = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c) * H + h) * D);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 x = km[d4];
+      acc = fmaf(x.x, s_q[4 * d4], acc);
+      acc = fmaf(x.y, s_q[4 * d4 + 1], acc);
+      acc = fmaf(x.z, s_q[4 * d4 + 2], acc);
+      acc = fmaf(x.w, s_q[4 * d4 + 3], acc);
+    }
+    keys[c] = order_key(acc);
+  }
+  select_topk(keys, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+}
+
+// ---------------------------------------------------------------------------
+// 2'. the same scores and top-k for kSelGroup query blocks of one segment and
+// head per workgroup, so that the segment's key means are read once per
+// group rather than once per query block (they are the kernel's whole memory
+// traffic).  Grid: H * ng_cap workgroups, (h, g) = (w / ng_cap, w % ng_cap),
+// g indexing groups of kSelGroup consecutive query blocks of a segment
+// (gprefix: exclusive prefix of ceil(blocks / kSelGroup) per segment);
+// workgroups past gprefix[n_seg] exit.  Key means go through LDS 32 rows at a
+// time with coalesced loads; each score is the same fmaf sequence over d as
+// in vsa_select_kernel, so scores and selections are bit-identical to it.
+// Dynamic LDS: kSelGroup * max_blocks keys.
+// ---------------------------------------------------------------------------
+constexpr int kSelGroup = 8;       // query blocks per workgroup
+constexpr int kSelChunk = 32;      // key-mean rows per LDS chunk
+constexpr int kSelPitch = 132;     // floats per LDS key-mean row (16-byte aligned, conflict-free b128 reads)
+
+__global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
+    const float* __restrict__ qmean, const float* __restrict__ kmean, const int32_t* __restrict__ bprefix,
+    const int32_t* __restrict__ gprefix, int n_seg, int H, int nb_cap, int ng_cap, int max_blocks, int topk,
+    float scale, int32_t* __restrict__ sel) {
+  constexpr int D = 128;
+  static_assert(kSelThreads == kSelGroup * kSelChunk, "one score per thread per chunk");
+  extern __shared__ float lds_f[];   // keys [kSelGroup][max_blocks] as uint32
+  __shared__ __attribute__((aligned(16))) float s_q[kSelGroup][D];
+  __shared__ __attribute__((aligned(16))) float s_k[kSelChunk][kSelPitch];
+  __shared__ int s_hist[256];
+  __shared__ int s_scan[kSelThreads];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+
+  const int64_t w = blockIdx.x;
+  const int h = (int)(w / ng_cap), g = (int)(w - (int64_t)h * ng_cap);
+  if (h >= H || g >= gprefix[n_seg]) return;
+  const int s = find_segment(gprefix, n_seg, g);
+  const int cb0 = bprefix[s];
+  const int nb_s = bprefix[s + 1] - cb0;
+  const int n_kb = min(nb_s, max_blocks);
+  const int qb0 = (g - gprefix[s]) * kSelGroup;            // first query block, relative to the segment
+  const int nq = min(kSelGroup, nb_s - qb0);
+  const int tid = threadIdx.x;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
+
+  // scaled query means of the group (rows past the group's end: zero, unused)
+  for (int i = tid; i < kSelGroup * D; i += kSelThreads) {
+    const int j = i / D, d = i - j * D;
+    s_q[j][d] = j < nq ? qmean[((int64_t)(cb0 + qb0 + j) * H + h) * D + d] * scale : 0.f;
+  }
+  // thread -> (query j, key row r of the chunk)
+  const int j = tid / kSelChunk, r = tid - j * kSelChunk;
+  for (int c0 = 0; c0 < n_kb; c0 += kSelChunk) {
+    __syncthreads();   // s_q written / previous chunk consumed
+    // 32 rows x 128 floats, 32 lanes per row: 512 contiguous bytes per row
+    for (int i = tid; i < kSelChunk * (D / 4); i += kSelThreads) {
+      const int rr = i / (D / 4), d4 = i - rr * (D / 4);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + rr < n_kb) x = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c0 + rr) * H + h) * D)[d4];
+      *reinterpret_cast<float4*>(&s_k[rr][4 * d4]) = x;
+    }
+    __syncthreads();
+    if (j < nq && c0 + r < n_kb) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 x = *reinterpret_cast<const float4*>(&s_k[r][4 * d4]);
+        const float4 y = *reinterpret_cast<const float4*>(&s_q[j][4 * d4]);
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+      }
+      keys[j * max_blocks + c0 + r] = order_key(acc);
+    }
+  }
+  for (int jj = 0; jj < nq; ++jj) {
+    __syncthreads();   // keys complete / previous selection's LDS use finished
+    int32_t* out = sel + ((int64_t)h * nb_cap + cb0 + qb0 + jj) * topk;
+    select_topk(keys + jj * max_blocks, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -486,28 +578,37 @@ int64_t vsa_num_blocks_bound(int64_t total_rows, int64_t n_seg) {
 
 size_t vsa_workspace_bytes(int64_t total_rows, int64_t n_seg, int64_t H) {
   const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
-  return align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256) +
-         2 * align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
+  const size_t prefix = align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256);
+  return 2 * prefix + 2 * align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
 }
 
 namespace {
 struct VsaWs {
-  int32_t* bprefix;
+  int32_t* bprefix;   // query/key blocks per segment, scanned
   float* qmean;
   float* kmean;
+  int32_t* gprefix;   // groups of kSelGroup blocks per segment, scanned
 };
 VsaWs carve(void* ws, int64_t total_rows, int64_t n_seg, int64_t H) {
   const int64_t nb_cap = vsa_num_blocks_bound(total_rows, n_seg);
+  const size_t prefix = align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256);
+  const size_t means = align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
   char* w = static_cast<char*>(ws);
   VsaWs r;
   r.bprefix = reinterpret_cast<int32_t*>(w);
-  w += align_up((size_t)(n_seg + 1) * 4, 256) + align_up(scan_workspace_bytes(n_seg + 1), 256);
+  w += prefix;
   r.qmean = reinterpret_cast<float*>(w);
-  w += align_up((size_t)(nb_cap > 0 ? nb_cap : 1) * H * 128 * 4, 256);
+  w += means;
   r.kmean = reinterpret_cast<float*>(w);
+  w += means;
+  r.gprefix = reinterpret_cast<int32_t*>(w);
   return r;
 }
 }  // namespace
+
+// Largest per-segment key-block count for the grouped selection: its keys
+// (kSelGroup * max_blocks * 4 bytes) and staging stay within 64 KB of LDS.
+constexpr int kSelGroupMaxBlocks = 1280;
 
 hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, int n_seg, int max_seqlen,
                              int total_rows, int H, bool bf16, int topk, float scale, int32_t* sel,
@@ -529,6 +630,17 @@ hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, in
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_blocks = (int)std::min<int64_t>(ceil_div(std::max(max_seqlen, 1), kVsaBlock), nb_cap);
+  if (max_blocks <= kSelGroupMaxBlocks) {
+    // groups of kSelGroup query blocks per segment (ceil(L / (64 * kSelGroup)) of them)
+    e = launch_build_tiles(cu, n_seg, total_rows, kVsaBlock * kSelGroup, w.gprefix, stream);
+    if (e != hipSuccess) return e;
+    const int64_t ng_cap = ceil_div(total_rows, kVsaBlock * kSelGroup) + n_seg;
+    if (ng_cap * H > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = (size_t)kSelGroup * max_blocks * 4;
+    vsa_select_group_kernel<<<(unsigned)(ng_cap * H), kSelThreads, lds, stream>>>(
+        qm, km, w.bprefix, w.gprefix, n_seg, H, (int)nb_cap, (int)ng_cap, max_blocks, topk, scale, sel);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)max_blocks * 4;
   vsa_select_kernel<<<(unsigned)(nb_cap * H), kSelThreads, lds, stream>>>(qm, km, w.bprefix, n_seg, H, (int)nb_cap,
                                                                          max_blocks, topk, scale, sel);
