@@ -91,6 +91,28 @@ def test_vsa_ragged_segments_means_selection_attention(topk):
     assert torch.isnan(o[rows:].float()).all()          # rows past total_rows untouched
 
 
+@pytest.mark.parametrize("topk", [3, 40])
+def test_vsa_grouped_and_per_block_selection_agree(topk):
+    # Up to 1,280 key blocks per segment the scores of 8 query blocks are
+    # formed together (key means read once per group); longer segments take
+    # one workgroup per query block.  max_seqlen is only an upper bound, so a
+    # larger one selects the per-block kernel on the same inputs: both must
+    # give the same selection bit for bit (same fmaf order per score), and it
+    # must pass the oracle check.  Segment lengths cover partial groups
+    # (1..7 blocks), exact groups (8, 16) and a long one (18 blocks = 8+8+2).
+    lengths = [1, 63, 64 * 8, 65, 0, 200, 64 * 16, 129, 64 * 17 + 5, 700]
+    H = 3
+    (q, k, v), cu, rows = _packed(lengths, H, seed=14, dup=(3, 5))
+    dq, dk = q.cuda(), k.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    grouped = h3.vsa_select(dq, dk, dcu, rows, topk, max_seqlen=max(lengths))
+    per_block = h3.vsa_select(dq, dk, dcu, rows, topk, max_seqlen=64 * 1281)
+    torch.cuda.synchronize()
+    assert torch.equal(grouped, per_block)
+    nb = oracle.block_layout(cu)[2][-1]
+    assert _check_selection(grouped[:, :nb].cpu().numpy(), W.to_f64(q[:rows]), W.to_f64(k[:rows]), cu, topk) > 0
+
+
 def test_vsa_exact_ties_break_to_lower_block():
     (q, k, v), cu, rows = _packed([64 * 6], 2, seed=12, dup=(1, 4))
     dcu = torch.from_numpy(cu).cuda()
