@@ -182,7 +182,10 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
  *
  * h3_vsa_attn_fwd: every row of query block b, head h, attends to the keys of
  * the blocks listed in sel[h][b] (entries < 0 end the list; blocks outside
- * b's segment are ignored): softmax over those keys only.  bf16, D = 128:
+ * b's segment are ignored; a block listed twice counts twice): softmax over
+ * those keys only.  The list may be in any order; the kernel visits it from a
+ * start that depends on the item's position in the launch (for L2
+ * locality), so results are deterministic for a given device.  bf16, D = 128:
  * the dense kernel's numerics (Q * scale * log2 e rounded to bf16 once, fp32
  * accumulation and softmax, bf16 P, one RNE rounding of O).  Rows
  * >= total_rows are neither read nor written.

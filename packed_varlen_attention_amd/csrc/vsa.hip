@@ -22,12 +22,14 @@
 //      list comes out in increasing block order;
 //   3. vsa_attn_kernel: one workgroup of 2 waves per (head, query block),
 //      32 query rows per wave; every kept block's K and V (64 keys x 256 B)
-//      goes HBM -> LDS by direct loads into one 32 KB stage, and the tile is
-//      consumed with the dense kernel's operand layout (Q pre-scaled by
-//      scale * log2 e in registers, S^T = K Q^T on 32x32x16 bf16 MFMA with
-//      -m folded into the accumulator input, transposed V reads, bf16 P).
-//      Four workgroups share a CU (LDS 32 KB, 256 VGPRs each), so one
-//      workgroup's loads overlap the others' MFMAs.
+//      goes HBM -> LDS by direct loads, in two 32-key halves double-buffered
+//      in 32 KB, and is consumed with the dense kernel's operand layout (Q
+//      pre-scaled by scale * log2 e in registers, S^T = K Q^T on 32x32x16
+//      bf16 MFMA with -m folded into the accumulator input, transposed V
+//      reads, bf16 P).  Four workgroups share a CU (LDS 32 KB, 256 VGPRs
+//      each).  Each item walks its kept blocks from a start position that
+//      keeps the workgroups resident on one XCD on neighbouring key blocks,
+//      so the XCD's L2 serves most of them (described above the kernel).
 #include "attn_common.h"
 
 namespace h3 {
@@ -353,18 +355,35 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
 // 3. block-sparse attention.  Grid: 8 * ceil(H * nb_cap / 8) workgroups of
 // 128 threads, head-major and cut into 8 contiguous chunks (one per XCD) like
 // the dense kernel; item w = (h, b) = (w / nb_cap, w % nb_cap).
+//
+// Key-block order (L2 locality).  A head's K/V (tens of MB) is far larger
+// than an XCD's L2, and with unrelated selections the workgroups resident on
+// one XCD, all of one head, would each sweep their kept blocks from the
+// first, at different phases, through the whole of it.  Instead each item
+// starts its (increasing) list at the first kept block at or after position
+// ((item index on the XCD) mod R) / R of the segment and wraps around, R
+// being the number of workgroups resident per XCD: items start in that order
+// one R-th of an item's run time apart, so at any moment the resident
+// workgroups sweep a common neighbourhood of key blocks, which the L2 then
+// holds.  The order depends only on the item, so results are deterministic;
+// softmax does not depend on the order up to rounding.
+//
+// Pipeline: the 64-key block is loaded in two 32-key halves, each into its
+// own K and V arrays; while one half is consumed, the other half's arrays
+// receive the next half (this block's second, the next block's first).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ bprefix,
-    const int32_t* __restrict__ sel, int n_seg, int H, int total_rows, int nb_cap, int topk,
+    const int32_t* __restrict__ sel, int n_seg, int H, int total_rows, int nb_cap, int topk, int resident,
     float scale_log2) {
   constexpr int D = 128;
   constexpr int NW = 2;                    // waves per workgroup
-  constexpr int DMA_ROWS = 64 / NW;        // tile rows each wave loads per tensor
-  constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
-  __shared__ __attribute__((aligned(1024))) char lk[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lv[kTileBytes];
+  constexpr int HALF_ROWS = 32 / NW;       // rows of a 32-key half each wave loads per tensor
+  constexpr int DMA_INSTR = HALF_ROWS / 4; // 4 rows (1 KB) per load instruction
+  // one array per half and tensor
+  __shared__ __attribute__((aligned(1024))) char lk0[kTileBytes / 2], lk1[kTileBytes / 2];
+  __shared__ __attribute__((aligned(1024))) char lv0[kTileBytes / 2], lv1[kTileBytes / 2];
 
   const int64_t W = (int64_t)H * nb_cap;
   const int64_t per = (W + 7) >> 3;
@@ -385,33 +404,95 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   const int64_t rs = (int64_t)H * D;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
-  // ---- direct HBM -> LDS loads of one 64-row block: wave w fills rows
-  // 32w .. 32w+31, four rows (1 KB) per instruction
-  // Byte offset (within the block) of the 16-byte chunk that the swizzle
-  // places in this lane's LDS slot for load tt, given the tile row it reads.
-  auto dma_off = [&](int tt, int row, bool is_v) __attribute__((always_inline)) {
-    const int trow = DMA_ROWS * wave + 4 * tt + (lane >> 4);
-    const int ch = (lane & 15) ^ (is_v ? swz_v(trow) : swz_k(trow));
-    return (uint32_t)row * row_bytes + (uint32_t)ch * 16u;
-  };
+  // ---- direct HBM -> LDS loads of one 32-key half: wave w fills rows
+  // 16w .. 16w+15 of the half, four rows (1 KB) per instruction; lane i
+  // writes LDS slot i, so it fetches the chunk that the swizzle places there.
+  // Full block: the lane's offset (its row among the instruction's four, its
+  // swizzled chunk) in a VGPR, the instruction's first row as the scalar
+  // offset.  The K swizzle depends on the row mod 16 (one VGPR per
+  // instruction), the V swizzle on the row mod 4 (one VGPR).
+  const int lrow = lane >> 4;
+  uint32_t koff_dma[DMA_INSTR];
+#pragma unroll
+  for (int tt = 0; tt < DMA_INSTR; ++tt)
+    koff_dma[tt] = (uint32_t)lrow * row_bytes + (uint32_t)(((lane & 15) ^ swz_k(4 * tt + lrow)) << 4);
+  const uint32_t voff_dma = (uint32_t)lrow * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
   const uint16_t* kh = k + (int64_t)h * D;
   const uint16_t* vh = v + (int64_t)h * D;
-  auto issue_block = [&](int kr0, int len) __attribute__((always_inline)) {
+  auto issue_half = [&](int kr0, int len, auto half_c) __attribute__((always_inline)) {
+    constexpr int half = decltype(half_c)::value;
+    char* dk = half ? lk1 : lk0;
+    char* dv = half ? lv1 : lv0;
     const int nrec = (int)(64u * row_bytes);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
+    if (__builtin_expect(len == kVsaBlock, 1)) {
 #pragma unroll
-    for (int tt = 0; tt < DMA_INSTR; ++tt) {
-      // ragged block: rows past its end repeat its last row
-      const int row = min(DMA_ROWS * wave + 4 * tt + (lane >> 4), len - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (DMA_ROWS * wave + 4 * tt) * 256), 16,
-                                               dma_off(tt, row, false), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (DMA_ROWS * wave + 4 * tt) * 256), 16,
-                                               dma_off(tt, row, true), 0, 0, 0);
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        const int row0 = 32 * half + HALF_ROWS * wave + 4 * tt;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + (HALF_ROWS * wave + 4 * tt) * 256), 16,
+                                                 koff_dma[tt], (int)(row0 * row_bytes), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + (HALF_ROWS * wave + 4 * tt) * 256), 16,
+                                                 voff_dma, (int)(row0 * row_bytes), 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        // ragged block: rows past its end repeat its last row
+        const uint32_t row = (uint32_t)min(32 * half + HALF_ROWS * wave + 4 * tt + lrow, len - 1);
+        const uint32_t kc = (uint32_t)(((lane & 15) ^ swz_k(4 * tt + lrow)) << 4);
+        const uint32_t vc = (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + (HALF_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + kc, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + (HALF_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + vc, 0, 0, 0);
+      }
     }
   };
+
+  // ---- kept-block list: its length (entries before the first negative)
+  // and the rotated start (entries below the start position), wave-uniform
+  const int32_t* my_sel = sel + ((int64_t)h * nb_cap + b) * topk;
+  const int seg_blocks = bprefix[s + 1] - cb0;
+  int n_list = topk, t0 = 0;
+  {
+    const int start = (int)(((int64_t)(jj % resident) * seg_blocks) / resident);
+    for (int base = 0; base < topk; base += 64) {
+      const int t = base + lane;
+      const int c = t < topk ? my_sel[t] : -1;
+      const uint64_t neg = __builtin_amdgcn_ballot_w64(c < 0);
+      const uint64_t below = __builtin_amdgcn_ballot_w64(c >= 0 && c - cb0 < start);
+      if (neg != 0) {
+        const int lim = __builtin_ctzll(neg);
+        n_list = base + lim;
+        t0 += __builtin_popcountll(below & ((1ull << lim) - 1));
+        break;
+      }
+      t0 += __builtin_popcountll(below);
+    }
+    n_list = __builtin_amdgcn_readfirstlane(n_list);
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    if (t0 >= n_list) t0 = 0;
+  }
+  // local block of the i-th entry in rotated order, -1 outside the segment
+  auto entry_block = [&](int i) __attribute__((always_inline)) -> int {
+    int t = t0 + i;
+    if (t >= n_list) t -= n_list;
+    const int cl = my_sel[__builtin_amdgcn_readfirstlane(t)] - cb0;
+    return (cl >= 0 && cl < seg_blocks) ? cl : -1;
+  };
+
+  // first valid entry: both its halves are requested before Q is loaded
+  int i = 0, cl = -1;
+  while (i < n_list && (cl = entry_block(i)) < 0) ++i;
+  int kr0 = seg_start + max(cl, 0) * kVsaBlock;
+  int len = min(kVsaBlock, seg_end - kr0);
+  if (i < n_list) {
+    issue_half(kr0, len, Int<0>{});
+    issue_half(kr0, len, Int<1>{});
+  }
 
   // ---- Q fragment (B operand) times scale * log2(e)
   bf16x8_t qf[8];
@@ -437,10 +518,10 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   {
     const int rl = 4 * g + ((lane & 15) >> 2);
     const int sv = swz_v(rl);
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int cl4 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
+      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl4 ^ (sv & 3))) << 4) + (lane & 1) * 8;
   }
 
   f32x16_t oacc[4];
@@ -450,27 +531,27 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   f32x16_t neg_m = f32x16_t{};
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute_s = [&](int half, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
+  auto compute_s = [&](const char* kl, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(lk + half * 8192 + koff[kc]);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + koff[kc]);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
                                                      0, 0, 0);
     }
   };
-  auto mask_tail = [&](f32x16_t& sacc, int key_rel, int len) __attribute__((always_inline)) {
+  auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
     if (key_rel + 32 > len) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= len) sacc[i] = -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int key = key_rel + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (key >= len) sacc[e] = -INFINITY;
       }
     }
   };
   auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
     float mx = sacc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
     return mx;
   };
   auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
@@ -487,68 +568,83 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
     }
     l_run = lsum;
   };
-  auto pv_half = [&](int half, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
+  auto pv_half = [&](const char* vl, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const char* vp = lv + half * 8192 + voff[db] + (16 * c) * 256;
+        const char* vp = vl + voff[db] + (16 * c) * 256;
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
       }
   };
-
-  const int32_t* my_sel = sel + ((int64_t)h * nb_cap + b) * topk;
-  const int seg_blocks = bprefix[s + 1] - cb0;
   bool first = true;
-  for (int t = 0; t < topk; ++t) {
-    const int c = my_sel[t];
-    if (c < 0) break;
-    const int cl = c - cb0;
-    if (cl < 0 || cl >= seg_blocks) continue;   // not a block of this segment: skipped
-    const int kr0 = seg_start + cl * kVsaBlock;
-    const int len = min(kVsaBlock, seg_end - kr0);
-    issue_block(kr0, len);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the block landed
-    __syncthreads();
-    // two 32-key halves, each: S, reference / rescale test, P, O += V P
+  // one 32-key half: S, reference / rescale test, P, O += V P
+  auto half_step = [&](const char* kl, const char* vl, int key_rel) __attribute__((always_inline)) {
+    f32x16_t sacc;
+    compute_s(kl, sacc, !first);
+    mask_tail(sacc, key_rel);
+    const float mloc = lane_max(sacc);
+    if (first) {
+      // the first half of the first kept block sets the reference
+      m_run = swap_halves_max(mloc);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x16_t sacc;
-      compute_s(half, sacc, !first);
-      mask_tail(sacc, 32 * half, len);
-      const float mloc = lane_max(sacc);
-      if (first) {
-        // the first half of the first kept block sets the reference
-        m_run = swap_halves_max(mloc);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] -= m_run;
-          neg_m[i] = -m_run;
-        }
-        first = false;
-      } else if (__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0) {
-        // rare: scores exceed the reference by more than 2^8
-        const float mpair = swap_halves_max(mloc);
-        const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-        m_run += delta;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] -= delta;
-          neg_m[i] = -m_run;
-        }
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] -= m_run;
+        neg_m[e] = -m_run;
       }
-      bf16x8_t pk[2];
-      exp_half(sacc, pk);
-      pv_half(half, pk);
+      first = false;
+    } else if (__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0) {
+      // rare: scores exceed the reference by more than 2^8
+      const float mpair = swap_halves_max(mloc);
+      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run += delta;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] -= delta;
+        neg_m[e] = -m_run;
+      }
     }
-    __syncthreads();                      // the stage is free for the next block
+    bf16x8_t pk[2];
+    exp_half(sacc, pk);
+    pv_half(vl, pk);
+  };
+  // Barrier without the workgroup fence of __syncthreads, which would wait
+  // for every tile load in flight: this wave's LDS reads complete first; the
+  // tile loads are waited for explicitly (vmcnt: this wave's) before it and
+  // by it (the other wave's).
+  auto bar = [&]() __attribute__((always_inline)) {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  while (i < n_list) {
+    int in = i + 1, cln = -1;
+    while (in < n_list && (cln = entry_block(in)) < 0) ++in;
+    const bool more = in < n_list;
+    const int kr0n = seg_start + max(cln, 0) * kVsaBlock;
+    const int lenn = min(kVsaBlock, seg_end - kr0n);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));   // half 0 landed; half 1 may be in flight
+    bar();
+    half_step(lk0, lv0, 0);
+    bar();                                                  // half 0's arrays are free
+    if (more) {
+      issue_half(kr0n, lenn, Int<0>{});
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR)); // half 1 landed; the next half 0 may be in flight
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    bar();
+    half_step(lk1, lv1, 32);
+    bar();                                                  // half 1's arrays are free
+    if (more) issue_half(kr0n, lenn, Int<1>{});
+    i = in;
+    len = lenn;
   }
 
   if (qrow < q_end && !first) {
@@ -657,9 +753,18 @@ hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, void* o,
   const int64_t grid = 8 * ceil_div(nb_cap * H, 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // workgroups resident per XCD: four per CU (32 KB of LDS and 2 waves of
+  // 256 VGPRs each), CUs spread evenly over the 8 XCDs
+  int dev = 0, n_cu = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int resident = std::max(1, n_cu / 8) * 4;
   vsa_attn_kernel<<<(unsigned)grid, 128, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<uint16_t*>(o), cu, w.bprefix, sel, n_seg, H, total_rows, (int)nb_cap, topk, scale_log2);
+      static_cast<uint16_t*>(o), cu, w.bprefix, sel, n_seg, H, total_rows, (int)nb_cap, topk, resident,
+      scale_log2);
   return hipGetLastError();
 }
 

@@ -172,3 +172,50 @@ def test_vsa_full_size_cube_grid_sampled():
             got = f64(o[64 * b:64 * b + 64, heads[hi]])
             assert np.abs(got - ref).max() <= 2e-2
             assert np.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 5e-3
+
+
+def test_vsa_attention_on_caller_lists():
+    """h3_vsa_attn_fwd on selection lists the caller made: any order, repeated
+    blocks (attended once per listing, as the oracle's key concatenation does),
+    blocks of other segments (ignored), and a negative entry that ends the list
+    before later entries.  Each workgroup starts its walk of the list at a
+    position tied to its index, so these lists also check that every entry is
+    visited exactly once whatever the start.  The expected output is the
+    oracle's attention on the lists reduced by the documented rules."""
+    lengths = [300, 64, 5, 700, 130]
+    H, topk = 3, 7
+    (q, k, v), cu, rows = _packed(lengths, H, seed=31)
+    _, bseg, bcu = oracle.block_layout(cu)
+    nb = int(bcu[-1])
+    nb_cap = h3.vsa_blocks_bound(rows, len(lengths))
+    rng = np.random.default_rng(5)
+    sel = np.full((H, nb_cap, topk), -1, np.int32)
+    ref_sel = np.full((H, nb, 2 * topk), -1, np.int32)
+    for h in range(H):
+        for b in range(nb):
+            s = int(bseg[b])
+            own = np.arange(bcu[s], bcu[s + 1])
+            others = np.setdiff1d(np.arange(nb), own)
+            lst = list(rng.permutation(own)[:rng.integers(1, min(len(own), topk) + 1)])
+            if rng.random() < 0.3:                     # a repeated block
+                lst.append(lst[0])
+            if len(others) and rng.random() < 0.5:     # a block of another segment
+                lst.insert(int(rng.integers(0, len(lst) + 1)), int(rng.choice(others)))
+            lst = lst[:topk]
+            if len(lst) < topk - 1 and rng.random() < 0.5:   # -1, then an entry that must be ignored
+                lst += [-1, int(own[0])]
+            sel[h, b, :len(lst)] = lst
+            kept = []
+            for c in lst:
+                if c < 0:
+                    break
+                if bcu[s] <= c < bcu[s + 1]:
+                    kept.append(c)
+            assert kept                                 # every list starts with a block of its own segment
+            ref_sel[h, b, :len(kept)] = kept
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.full_like(dq, float("nan"))
+    h3.vsa_attn_fwd(dq, dk, dv, torch.from_numpy(cu).cuda(), rows, torch.from_numpy(sel).cuda(), topk, o=o)
+    torch.cuda.synchronize()
+    ref = oracle.vsa_attention(W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows]), cu, ref_sel)
+    assert_close(o[:rows], ref, "bf16", "VSA attention on caller-made lists")
