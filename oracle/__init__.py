@@ -34,6 +34,19 @@ Steps and the passages they follow:
                   velocity to clean estimate, eta = 0 Euler step with separate
                   video / audio sigma schedules, re-pin of anchor rows); the
                   deployment page's 50 sigma points and flow shifts 12 / 3
+  e4m3_value,
+  e4m3_round,
+  mx_exponent,
+  quantize_mx_e4m3,
+  dequantize_mx_e4m3,
+  fp8qk_inputs,
+  attention_base2,
+  attention_fp8qk [P1] section 五 keeps the active DiT block in FP8 and section
+                  六 names a SAGE attention operator, with no algorithm for
+                  low-precision attention: the reading taken is
+                  MX block-scaled E4M3 Q and K (OCP 8-bit floating point and
+                  Microscaling format definitions), the plain attention on the
+                  dequantized values
 
 Pinning (tests/test_oracle.py): the page's cu_seqlens example and exact zeros,
 brute force in pure Python, torch's float64 scaled_dot_product_attention per
@@ -50,9 +63,13 @@ permuting keys inside a kept block.  No function here is "parity unpinned".
 from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
                         attention, attention_rows, attention_weights, unpack, run,
                         rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler,
-                        block_layout, block_means, vsa_scores, vsa_select, vsa_attention)
+                        block_layout, block_means, vsa_scores, vsa_select, vsa_attention,
+                        E4M3_MAX, e4m3_value, e4m3_round, mx_exponent, quantize_mx_e4m3,
+                        dequantize_mx_e4m3, fp8qk_inputs, attention_base2, attention_fp8qk)
 
 __all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
            "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk",
            "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler",
-           "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention"]
+           "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention",
+           "E4M3_MAX", "e4m3_value", "e4m3_round", "mx_exponent", "quantize_mx_e4m3",
+           "dequantize_mx_e4m3", "fp8qk_inputs", "attention_base2", "attention_fp8qk"]

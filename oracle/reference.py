@@ -282,6 +282,137 @@ def vsa_attention(q, k, v, cu, sel, block: int = 64, softmax_scale: Optional[flo
 
 
 # ---------------------------------------------------------------------------
+# FP8 Q.K attention.  [P1] section 五 keeps the DiT block being computed in
+# FP8 and section 六 names a SAGE attention operator, but the pages give no
+# low-precision attention algorithm; this is the reading taken: Q (times softmax_scale * log2 e) and K are stored as E4M3 values with
+# one power-of-two scale per 32 consecutive channels of a row (the OCP
+# Microscaling format MXFP8 with block 32), V stays as given, and attention is
+# the plain definition applied to the dequantized Q and K, with base-2
+# exponentials (the log2 e factor already sits in Q).
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP OFP8 E4M3 code: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 is subnormal (m / 8 * 2^-6); no
+    infinities; S.1111.111 is NaN."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def _e4m3_table():
+    mags = np.array([e4m3_value(c) for c in range(0x7F)], np.float64)   # codes 0x00..0x7E, increasing
+    return mags
+
+
+def e4m3_round(x):
+    """E4M3 code(s) of the value nearest to x (|x| <= 448), ties to the code
+    with an even mantissa; the sign bit is x's (so tiny negatives give -0).
+    Scalar in, int out; array in, uint8 array out."""
+    arr = np.asarray(x, np.float64)
+    if not (np.abs(arr) <= E4M3_MAX).all():
+        raise ValueError("outside the E4M3 range")
+    mags = _e4m3_table()
+    a = np.abs(arr)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)   # first magnitude >= a
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == mags[hi], hi, pick)
+    code = pick.astype(np.int64) | np.where(np.signbit(arr), 0x80, 0)
+    if np.ndim(x) == 0:
+        return int(code)
+    return code.astype(np.uint8)
+
+
+def mx_exponent(amax: float) -> int:
+    """Shared block exponent: the smallest integer e with amax <= 448 * 2^e, so
+    that no element of the block needs saturating (the OCP spec's own rule,
+    floor(log2 amax) - 8 with saturation, is not used); -127 for an all-zero
+    block; clamped to the E8M0 range [-127, 127]."""
+    if amax == 0.0:
+        return -127
+    e = math.ceil(math.log2(amax / E4M3_MAX))
+    while amax > E4M3_MAX * 2.0 ** e:          # guard the log's rounding
+        e += 1
+    while e > -127 and amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return max(-127, min(127, e))
+
+
+def quantize_mx_e4m3(x, block: int = 32):
+    """MX block quantization of float32 values x [..., D] (D a multiple of
+    `block`): returns (codes uint8 [..., D], exponents int32 [..., D/block])
+    with x ~ e4m3_value(code) * 2^exponent.  The scaled value x * 2^-e is
+    formed in float32 (exact for the exponents that occur) and rounded to
+    E4M3 once."""
+    x = np.asarray(x, np.float32)
+    shp = x.shape
+    D = shp[-1]
+    xb = x.reshape(-1, D // block, block)
+    amax = np.abs(xb).max(axis=-1).astype(np.float64)
+    exps = np.array([mx_exponent(float(m)) for m in amax.ravel()], np.int32).reshape(amax.shape)
+    f = np.ldexp(np.float32(1.0), -exps).astype(np.float32)              # 2^-e, exact in float32
+    scaled = (xb * f[..., None]).astype(np.float32)
+    codes = e4m3_round(scaled.astype(np.float64))
+    return codes.reshape(shp), exps.reshape(shp[:-1] + (D // block,))
+
+
+def dequantize_mx_e4m3(codes, exps, block: int = 32):
+    """float64 values of MX E4M3 data: e4m3_value(code) * 2^exponent."""
+    codes = np.asarray(codes)
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    vals = table[codes.astype(np.int64)]
+    scale = np.repeat(np.ldexp(1.0, np.asarray(exps, np.int64)), block, axis=-1)
+    return vals * scale
+
+
+def fp8qk_inputs(q, k, softmax_scale: Optional[float] = None):
+    """The quantized operands of FP8 Q.K attention: Q multiplied by
+    float32(softmax_scale * log2 e) in float32, then Q and K (given as
+    float32-representable values) MX-quantized.  Returns
+    (q_codes, q_exps, k_codes, k_exps)."""
+    D = q.shape[-1]
+    c = np.float32(_scale(D, softmax_scale) * 1.4426950408889634)
+    qs = np.asarray(q, np.float32) * c
+    qc, qe = quantize_mx_e4m3(qs)
+    kc, ke = quantize_mx_e4m3(np.asarray(k, np.float32))
+    return qc, qe, kc, ke
+
+
+def attention_base2(qh, kh, v, cu, row_block: int = 1024):
+    """O[i,h] = sum_j 2^(s_ij - max_j s_ij) V[j,h] / sum_j 2^(s_ij - max), with
+    s_ij = qh[i,h] . kh[j,h] over the keys of i's segment: the plain
+    definition of attention with logits already in base-2 units."""
+    rows, H, D = qh.shape
+    o = np.zeros((rows, H, v.shape[-1]), np.float64)
+    for a, b in zip(np.asarray(cu[:-1], np.int64), np.asarray(cu[1:], np.int64)):
+        if b <= a:
+            continue
+        for h in range(H):
+            for r0 in range(a, b, row_block):
+                r1 = min(b, r0 + row_block)
+                S = qh[r0:r1, h, :] @ kh[a:b, h, :].T
+                P = np.exp2(S - S.max(axis=1, keepdims=True))
+                o[r0:r1, h, :] = (P / P.sum(axis=1, keepdims=True)) @ v[a:b, h, :]
+    return o
+
+
+def attention_fp8qk(q, k, v, cu, softmax_scale: Optional[float] = None):
+    """FP8 Q.K attention: the plain definition on the dequantized operands of
+    fp8qk_inputs, base-2 exponentials."""
+    qc, qe, kc, ke = fp8qk_inputs(q, k, softmax_scale)
+    return attention_base2(dequantize_mx_e4m3(qc, qe), dequantize_mx_e4m3(kc, ke), np.asarray(v, np.float64), cu)
+
+
+# ---------------------------------------------------------------------------
 # denoising-step epilogue ([P1] section 四, the runtime loop: stage 5 turns
 # the rectified-flow velocity into a clean estimate, stage 6 is the
 # deterministic Euler solver with eta = 0 stepping video and audio by their

@@ -566,3 +566,120 @@ def test_vsa_key_permutation_inside_a_kept_block():
     o2 = oracle.vsa_attention(q, k[perm], v[perm], cu, sel)     # block means and key sets unchanged
     assert np.array_equal(oracle.vsa_select(q, k[perm], cu, topk=2), sel)
     assert np.allclose(o, o2, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# FP8 Q.K attention: E4M3 values, rounding, MX block exponents, quantization,
+# and the attention on dequantized operands
+# ---------------------------------------------------------------------------
+def test_e4m3_values_from_the_format_definition():
+    # OCP 8-bit floating point E4M3: bias 7, max normal S.1111.110 = 448,
+    # min normal 2^-6, min subnormal 2^-9, S.1111.111 = NaN, no infinities
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0xFE) == -448.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x38) == 1.0 and oracle.e4m3_value(0x40) == 2.0
+    assert oracle.e4m3_value(0x3C) == 1.5 and oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    assert oracle.e4m3_value(0x80) == 0.0 and math.copysign(1.0, oracle.e4m3_value(0x80)) < 0
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))            # codes 0x00..0x7E increase
+    assert all(oracle.e4m3_value(c | 0x80) == -oracle.e4m3_value(c) for c in range(0x7F))
+    # spacing: 8 values per binade, ulp 2^(e-3); subnormals spaced 2^-9
+    for e in range(-6, 9):
+        grid = [v for v in pos if 2.0 ** e <= v < 2.0 ** (e + 1)]
+        assert len(grid) == (8 if e < 8 else 7) and np.allclose(np.diff(grid), 2.0 ** (e - 3))
+
+
+def test_e4m3_round_nearest_ties_to_even():
+    for c in range(256):
+        if c not in (0x7F, 0xFF):
+            assert oracle.e4m3_round(oracle.e4m3_value(c)) == c   # every finite code round-trips
+    # midpoints go to the even mantissa: 1.0625 between 1.0 (m=0) and 1.125 (m=1);
+    # 1.1875 between 1.125 (m=1) and 1.25 (m=2); 432 between 416 (m=5) and 448 (m=6);
+    # 2^-10 between 0 and the smallest subnormal
+    assert oracle.e4m3_round(1.0625) == 0x38
+    assert oracle.e4m3_round(1.1875) == 0x3A
+    assert oracle.e4m3_round(432.0) == 0x7E and oracle.e4m3_round(-432.0) == 0xFE
+    assert oracle.e4m3_round(2.0 ** -10) == 0x00 and oracle.e4m3_round(-(2.0 ** -10)) == 0x80
+    assert oracle.e4m3_round(1.0625 + 1e-9) == 0x39 and oracle.e4m3_round(1.0625 - 1e-9) == 0x38
+    # nearest value against a sorted table searched independently
+    table = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    rng = np.random.default_rng(3)
+    for x in np.concatenate([rng.uniform(-448, 448, 300), rng.standard_normal(300) * 0.01]):
+        got = oracle.e4m3_value(oracle.e4m3_round(x))
+        j = np.searchsorted(table, abs(x))
+        cand = table[max(j - 1, 0):j + 1]
+        assert abs(abs(got) - abs(x)) == np.abs(cand - abs(x)).min()
+        assert math.copysign(1.0, got) == math.copysign(1.0, x)
+    with pytest.raises(ValueError):
+        oracle.e4m3_round(449.0)
+
+
+def test_mx_exponent_closed_form():
+    # the smallest e with amax <= 448 * 2^e: then amax * 2^-e lies in (224, 448]
+    assert oracle.mx_exponent(448.0) == 0 and oracle.mx_exponent(448.0001) == 1
+    assert oracle.mx_exponent(224.0) == -1 and oracle.mx_exponent(224.0001) == 0
+    assert oracle.mx_exponent(1.0) == -8 and oracle.mx_exponent(0.0) == -127
+    rng = np.random.default_rng(4)
+    for amax in np.exp(rng.uniform(-60, 60, 500)):
+        e = oracle.mx_exponent(float(amax))
+        assert 224.0 < amax * 2.0 ** -e <= 448.0
+
+
+def test_mx_quantization_error_bound_and_exact_grid():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((5, 3, 128)) * np.exp(rng.uniform(-8, 8, (5, 3, 1)))).astype(np.float32)
+    x[0, 0, :32] = 0.0                                   # an all-zero block
+    codes, exps = oracle.quantize_mx_e4m3(x)
+    assert codes.shape == x.shape and exps.shape == (5, 3, 4)
+    assert (exps[0, 0, 0] == -127) and (codes[0, 0, :32] & 0x7F == 0).all()
+    deq = oracle.dequantize_mx_e4m3(codes, exps)
+    scale = np.repeat(np.ldexp(1.0, exps.astype(np.int64)), 32, axis=-1)
+    xs = np.abs(x.astype(np.float64)) / scale             # the block-scaled magnitudes, <= 448
+    assert xs.max() <= 448.0
+    err = np.abs(deq - x)
+    normal = xs >= 2.0 ** -6
+    # half an ulp: 3 mantissa bits give 2^-4 relative for normals, 2^-10 * scale below
+    assert (err[normal] <= 2.0 ** -4 * np.abs(x[normal]) + 0.0).all()
+    assert (err[~normal] <= 2.0 ** -10 * scale[~normal]).all()
+    # values already on a block's grid come back unchanged
+    g = rng.choice([c for c in range(0x7F) if oracle.e4m3_value(c) <= 256.0], size=(2, 2, 128))
+    y = np.array([[[oracle.e4m3_value(c) for c in r] for r in m] for m in g]) * 2.0 ** -8
+    y[..., ::32] = 1.0                                    # amax 1.0 in every block: exponent -8
+    yc, ye = oracle.quantize_mx_e4m3(y)
+    assert (ye == -8).all() and np.array_equal(oracle.dequantize_mx_e4m3(yc, ye), y)
+
+
+def test_fp8qk_attention_reduces_to_plain_attention_on_grid_values():
+    # softmax_scale = 1 / log2(e) makes the Q factor scale * log2 e exactly 1 in
+    # float32; with Q and K on an MX grid the quantization is exact, and base-2
+    # exponentials of the logits are the natural softmax at scale ln 2
+    rng = np.random.default_rng(9)
+    cands = [c for c in range(0x7F) if oracle.e4m3_value(c) <= 256.0]
+    def grid(rows):
+        g = rng.choice(cands, size=(rows, 2, 64)) | (rng.integers(0, 2, (rows, 2, 64)) << 7)
+        y = np.vectorize(oracle.e4m3_value)(g) * 2.0 ** -8
+        y[..., ::32] = 1.0
+        return y
+    rows = 150
+    q, k = grid(rows), grid(rows)
+    v = rng.standard_normal((rows, 2, 64))
+    cu = np.array([0, 37, 37, 150])
+    s = 1.0 / 1.4426950408889634
+    assert np.float32(s * 1.4426950408889634) == np.float32(1.0)
+    got = oracle.attention_fp8qk(q, k, v, cu, softmax_scale=s)
+    want = oracle.attention(q, k, v, cu, softmax_scale=math.log(2.0))
+    assert np.allclose(got, want, atol=1e-12, rtol=0)
+
+
+def test_fp8qk_attention_error_against_exact_attention():
+    # E4M3's 3 mantissa bits bound the logit error; on this workload's
+    # N(0, 0.25) rows the output stays within a few percent of exact attention
+    rng = np.random.default_rng(10)
+    q, k, v = (rng.standard_normal((300, 2, 128)) * 0.5 for _ in range(3))
+    cu = np.array([0, 300])
+    got = oracle.attention_fp8qk(q.astype(np.float32), k.astype(np.float32), v, cu)
+    want = oracle.attention(q.astype(np.float32).astype(np.float64), k.astype(np.float32).astype(np.float64), v, cu)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert 1e-4 < rel < 5e-2
