@@ -137,6 +137,43 @@ h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Attention with FP8 Q and K.  [P1] section 五 keeps the DiT block being
+ * computed in FP8 and section 六 names a SAGE attention operator; the pages
+ * give no low-precision attention algorithm.  This pair implements one
+ * reading: Q (times softmax_scale * log2 e) and K stored as OCP E4M3 values
+ * with one power-of-two scale per 32 consecutive channels of a row (the
+ * MXFP8 layout of the OCP Microscaling format), V and P.V in bf16, and
+ * attention the plain definition on the dequantized Q and K (the same
+ * segment rules as h3_varlen_attn_fwd).  It trades accuracy for speed:
+ * against unquantized attention the output differs by ~1e-2 relative RMS on
+ * N(0, 0.25) inputs (E4M3 keeps 3 mantissa bits), against attention on the
+ * dequantized values by bf16 rounding only.
+ *
+ * h3_quantize_qk_fp8: for every row r < rows, head h and block j of 32
+ * channels, with x = Q * float32(float32(scale) * log2 e) (products in fp32)
+ * or x = K: e = the smallest integer with max|x| <= 448 * 2^e (-127 for an
+ * all-zero block, clamped to [-127, 127]), exponent byte e + 127, and each
+ * code the E4M3 value nearest to x * 2^-e, ties to even mantissa, sign bit
+ * from x.  softmax_scale 0 means 1/sqrt(D).
+ *
+ *   q, k     : packed bf16 [>= rows][H][128] (device, 16-byte aligned)
+ *   q8, k8   : uint8 codes [rows][H][128] out (16-byte aligned)
+ *   qe, ke   : uint8 exponent bytes [rows][H][4] out (4-byte aligned)
+ *
+ * h3_varlen_attn_fwd_fp8qk: O as h3_varlen_attn_fwd with scores
+ * dequant(q8, qe) . dequant(k8, ke) in base-2 units (exp2), V bf16
+ * [>= total_rows][H][128], O bf16 out; the workspace is the dense call's
+ * (h3_attn_workspace_bytes).  Only bf16 and D = 128 (H3_ERR_UNSUPPORTED
+ * otherwise). */
+h3_status h3_quantize_qk_fp8(const void* q, const void* k, int32_t rows, int32_t H, int32_t D, h3_dtype dt,
+                             float softmax_scale, uint8_t* q8, uint8_t* qe, uint8_t* k8, uint8_t* ke,
+                             hipStream_t stream);
+h3_status h3_varlen_attn_fwd_fp8qk(const uint8_t* q8, const uint8_t* qe, const uint8_t* k8, const uint8_t* ke,
+                                   const void* v, const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
+                                   int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, void* o,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Unpack by modality ([P1] section 三: the output sequence is sliced by
  * modality into per-modality velocities; [P3] window-aligned SP: token order
  * restored after attention).

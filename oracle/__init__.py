@@ -41,6 +41,7 @@ Steps and the passages they follow:
   dequantize_mx_e4m3,
   fp8qk_inputs,
   attention_base2,
+  attention_base2_rows,
   attention_fp8qk [P1] section 五 keeps the active DiT block in FP8 and section
                   六 names a SAGE attention operator, with no algorithm for
                   low-precision attention: the reading taken is
@@ -65,11 +66,13 @@ from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply
                         rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler,
                         block_layout, block_means, vsa_scores, vsa_select, vsa_attention,
                         E4M3_MAX, e4m3_value, e4m3_round, mx_exponent, quantize_mx_e4m3,
-                        dequantize_mx_e4m3, fp8qk_inputs, attention_base2, attention_fp8qk)
+                        dequantize_mx_e4m3, fp8qk_inputs, attention_base2, attention_base2_rows,
+                        attention_fp8qk)
 
 __all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
            "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk",
            "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler",
            "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention",
            "E4M3_MAX", "e4m3_value", "e4m3_round", "mx_exponent", "quantize_mx_e4m3",
-           "dequantize_mx_e4m3", "fp8qk_inputs", "attention_base2", "attention_fp8qk"]
+           "dequantize_mx_e4m3", "fp8qk_inputs", "attention_base2", "attention_base2_rows",
+           "attention_fp8qk"]

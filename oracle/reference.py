@@ -375,12 +375,13 @@ def dequantize_mx_e4m3(codes, exps, block: int = 32):
 
 
 def fp8qk_inputs(q, k, softmax_scale: Optional[float] = None):
-    """The quantized operands of FP8 Q.K attention: Q multiplied by
-    float32(softmax_scale * log2 e) in float32, then Q and K (given as
-    float32-representable values) MX-quantized.  Returns
-    (q_codes, q_exps, k_codes, k_exps)."""
+    """The quantized operands of FP8 Q.K attention: Q multiplied in float32 by
+    c = float32(float32(softmax_scale) * log2 e) (the scale is a float32
+    argument; the product with log2 e is formed in float64 and rounded once),
+    then Q and K (given as float32-representable values) MX-quantized.
+    Returns (q_codes, q_exps, k_codes, k_exps)."""
     D = q.shape[-1]
-    c = np.float32(_scale(D, softmax_scale) * 1.4426950408889634)
+    c = np.float32(np.float64(np.float32(_scale(D, softmax_scale))) * 1.4426950408889634)
     qs = np.asarray(q, np.float32) * c
     qc, qe = quantize_mx_e4m3(qs)
     kc, ke = quantize_mx_e4m3(np.asarray(k, np.float32))
@@ -403,6 +404,25 @@ def attention_base2(qh, kh, v, cu, row_block: int = 1024):
                 P = np.exp2(S - S.max(axis=1, keepdims=True))
                 o[r0:r1, h, :] = (P / P.sum(axis=1, keepdims=True)) @ v[a:b, h, :]
     return o
+
+
+def attention_base2_rows(qh, kh, v, cu, rows: Sequence[int], heads: Optional[Sequence[int]] = None):
+    """attention_base2 evaluated only for the packed rows `rows` and heads
+    `heads`: float64 [len(rows), len(heads), Dv]."""
+    rows = np.asarray(rows, np.int64)
+    H = qh.shape[1]
+    heads = np.arange(H) if heads is None else np.asarray(heads, np.int64)
+    cu = np.asarray(cu, np.int64)
+    out = np.zeros((rows.shape[0], heads.shape[0], v.shape[-1]), np.float64)
+    seg_of = np.searchsorted(cu, rows, side="right") - 1
+    for s in np.unique(seg_of):
+        a, b = cu[s], cu[s + 1]
+        sel = np.nonzero(seg_of == s)[0]
+        for hi, h in enumerate(heads):
+            S = qh[rows[sel], h, :] @ kh[a:b, h, :].T
+            P = np.exp2(S - S.max(axis=1, keepdims=True))
+            out[sel, hi, :] = (P / P.sum(axis=1, keepdims=True)) @ v[a:b, h, :]
+    return out
 
 
 def attention_fp8qk(q, k, v, cu, softmax_scale: Optional[float] = None):

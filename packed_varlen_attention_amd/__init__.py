@@ -28,10 +28,12 @@ from ._lib import (H3Error, H3_BF16, H3_F32, TEXT, VIDEO, AUDIO, LIB_PATH, SIGNA
                    status_string, version, pack_rope, varlen_attn_fwd, unpack_by_modality,
                    unpack_euler, sigma_schedule, vsa_blocks_bound, vsa_select, vsa_attn_fwd,
                    validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
-                   unpack_workspace_bytes, workspace, rope_cfg, probe_mfma_bf16)
+                   unpack_workspace_bytes, workspace, rope_cfg, probe_mfma_bf16, quantize_qk_fp8,
+                   varlen_attn_fwd_fp8qk)
 
 __all__ = ["H3Error", "H3_BF16", "H3_F32", "TEXT", "VIDEO", "AUDIO", "LIB_PATH", "SIGNATURES",
            "load", "status_string", "version", "pack_rope", "varlen_attn_fwd",
            "unpack_by_modality", "unpack_euler", "sigma_schedule", "vsa_blocks_bound", "vsa_select",
            "vsa_attn_fwd", "validate_seqlens", "pack_workspace_bytes",
-           "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg", "probe_mfma_bf16"]
+           "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg", "probe_mfma_bf16",
+           "quantize_qk_fp8", "varlen_attn_fwd_fp8qk"]

@@ -53,6 +53,9 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
     "h3_vsa_attn_fwd": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _c.c_int, _f32, _vp, _i32,
                                    _vp, _vp, _sz, _vp]),
+    "h3_quantize_qk_fp8": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _c.c_int, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "h3_varlen_attn_fwd_fp8qk": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            _c.c_int, _vp, _vp, _sz, _vp]),
     "h3_validate_seqlens": (_c.c_int, [_vp, _i32, _i32, _vp]),
     "h3_probe_mfma_bf16": (_c.c_int, [_i32, _i32, _vp, _vp]),
     "h3_status_string": (_c.c_char_p, [_c.c_int]),
@@ -221,6 +224,61 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, total_rows: int, max_seqlen: int = 0,
                                 int(total_rows), H, D, _dt(q), float(softmax_scale), _ptr(o),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "h3_varlen_attn_fwd")
+    return o
+
+
+def quantize_qk_fp8(q, k, rows: int, softmax_scale: float = 0.0, *, q8=None, qe=None, k8=None, ke=None,
+                    stream=None):
+    """h3_quantize_qk_fp8 on packed bf16 [>= rows, H, 128] Q and K.  Returns
+    (q8, qe, k8, ke): uint8 codes [rows, H, 128] and exponent bytes
+    [rows, H, 4]."""
+    torch = _torch()
+    lib = load()
+    _, H, D = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    if rows > q.shape[0]:
+        raise ValueError("rows exceeds the tensors' rows")
+    mk = lambda n: torch.empty((max(rows, 1), H, n), dtype=torch.uint8, device=q.device)
+    q8 = mk(D) if q8 is None else q8
+    k8 = mk(D) if k8 is None else k8
+    qe = mk(D // 32) if qe is None else qe
+    ke = mk(D // 32) if ke is None else ke
+    for t in (q8, k8, qe, ke):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise TypeError("codes and exponents must be contiguous uint8")
+    if q8.numel() < rows * H * D or k8.numel() < rows * H * D or qe.numel() < rows * H * (D // 32) \
+            or ke.numel() < rows * H * (D // 32):
+        raise ValueError("output buffers too small")
+    st = lib.h3_quantize_qk_fp8(_ptr(q), _ptr(k), int(rows), H, D, _dt(q), float(softmax_scale), _ptr(q8),
+                                _ptr(qe), _ptr(k8), _ptr(ke), _stream(stream))
+    _check(st, "h3_quantize_qk_fp8")
+    return q8, qe, k8, ke
+
+
+def varlen_attn_fwd_fp8qk(q8, qe, k8, ke, v, cu_seqlens, total_rows: int, max_seqlen: int = 0, *, o=None,
+                          ws=None, stream=None):
+    """h3_varlen_attn_fwd_fp8qk: attention on MX-E4M3 Q and K (from
+    quantize_qk_fp8) with bf16 V [>= total_rows, H, 128].  Returns o."""
+    torch = _torch()
+    lib = load()
+    rows, H, D = v.shape
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if total_rows > rows or q8.shape[0] < total_rows or k8.shape[0] < total_rows:
+        raise ValueError("total_rows exceeds the tensors' rows")
+    if tuple(q8.shape[1:]) != (H, D) or tuple(k8.shape[1:]) != (H, D) or tuple(qe.shape[1:]) != (H, D // 32) \
+            or tuple(ke.shape[1:]) != (H, D // 32):
+        raise ValueError("codes [rows, H, D] and exponents [rows, H, D/32] must match V's heads")
+    n_seg = cu_seqlens.shape[0] - 1
+    if o is None:
+        o = torch.empty_like(v)
+    if ws is None:
+        ws = workspace(lib.h3_attn_workspace_bytes(total_rows, n_seg), v.device)
+    st = lib.h3_varlen_attn_fwd_fp8qk(_ptr(q8), _ptr(qe), _ptr(k8), _ptr(ke), _ptr(v), _ptr(cu_seqlens), n_seg,
+                                      int(max_seqlen), int(total_rows), H, D, _dt(v), _ptr(o), _ptr(ws),
+                                      ws.numel(), _stream(stream))
+    _check(st, "h3_varlen_attn_fwd_fp8qk")
     return o
 
 

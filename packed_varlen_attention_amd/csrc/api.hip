@@ -129,6 +129,40 @@ h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
                                       n_seg, total_rows, H, D, scale, workspace, stream));
 }
 
+h3_status h3_quantize_qk_fp8(const void* q, const void* k, int32_t rows, int32_t H, int32_t D, h3_dtype dt,
+                             float softmax_scale, uint8_t* q8, uint8_t* qe, uint8_t* k8, uint8_t* ke,
+                             hipStream_t stream) {
+  if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
+  if (dt != H3_BF16 || D != 128) return H3_ERR_UNSUPPORTED;
+  if (H <= 0 || H > kMaxHeads || rows < 0 || rows > kMaxRows) return H3_ERR_SHAPE;
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale)) return H3_ERR_UNSUPPORTED;
+  if (rows == 0) return H3_OK;
+  if (!q || !k || !q8 || !qe || !k8 || !ke) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(k8) ||
+      (reinterpret_cast<uintptr_t>(qe) & 3u) || (reinterpret_cast<uintptr_t>(ke) & 3u))
+    return H3_ERR_ALIGN;
+  const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)D));
+  return from_hip(h3::launch_quantize_qk_fp8(q, k, rows, H, scale, q8, k8, qe, ke, stream));
+}
+
+h3_status h3_varlen_attn_fwd_fp8qk(const uint8_t* q8, const uint8_t* qe, const uint8_t* k8, const uint8_t* ke,
+                                   const void* v, const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
+                                   int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, void* o,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
+  if (dt != H3_BF16 || D != 128) return H3_ERR_UNSUPPORTED;
+  if (H <= 0 || H > kMaxHeads) return H3_ERR_SHAPE;
+  if (n_seg < 0 || total_rows < 0 || max_seqlen < 0 || total_rows > kMaxRows) return H3_ERR_SHAPE;
+  if (total_rows == 0 || n_seg == 0) return H3_OK;
+  if (!q8 || !qe || !k8 || !ke || !v || !o || !cu_seqlens) return H3_ERR_NULL;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(qe) & 3u) || (reinterpret_cast<uintptr_t>(ke) & 3u))
+    return H3_ERR_ALIGN;
+  if (!workspace || workspace_bytes < h3::attn_workspace_bytes(total_rows, n_seg)) return H3_ERR_WORKSPACE;
+  return from_hip(h3::launch_attn_fp8qk(q8, qe, k8, ke, v, o, cu_seqlens, n_seg, total_rows, H, workspace,
+                                        stream));
+}
+
 size_t h3_unpack_workspace_bytes(int32_t n) {
   if (n < 0) return 0;
   return h3::unpack_workspace_bytes(n);

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
@@ -212,3 +212,22 @@ def test_probe_host_validation(lib):
     assert lib.h3_probe_mfma_bf16(512, 0, 0x1000, None) == 3
     assert lib.h3_probe_mfma_bf16((1 << 20) + 1, 10, 0x1000, None) == 3
     assert lib.h3_probe_mfma_bf16(1 << 10, (1 << 18) + 1, 0x1000, None) == 3   # > 2^28 workgroup-iterations
+
+
+def test_fp8qk_host_validation(lib):
+    qz = lib.h3_quantize_qk_fp8
+    at = lib.h3_varlen_attn_fwd_fp8qk
+    def Q(q=P, k=P, rows=300, H=4, D=128, dt=0, scale=0.0, q8=P, qe=P, k8=P, ke=P):
+        return qz(q, k, rows, H, D, dt, scale, q8, qe, k8, ke, None)
+    def A(q8=P, qe=P, k8=P, ke=P, v=P, cu=P, n_seg=2, max_seqlen=256, rows=300, H=4, D=128, dt=0, o=P,
+          ws=P, wsb=1 << 30):
+        return at(q8, qe, k8, ke, v, cu, n_seg, max_seqlen, rows, H, D, dt, o, ws, wsb, None)
+    assert Q(dt=7) == DTYPE and A(dt=7) == DTYPE
+    assert Q(dt=1) == UNSUPPORTED and A(dt=1) == UNSUPPORTED      # bf16 only
+    assert Q(D=64) == UNSUPPORTED and A(D=64) == UNSUPPORTED      # head dim 128 only
+    assert Q(H=0) == SHAPE and A(H=0) == SHAPE and Q(rows=-1) == SHAPE and A(rows=-1) == SHAPE
+    assert Q(scale=-1.0) == UNSUPPORTED and Q(scale=float("nan")) == UNSUPPORTED
+    assert Q(q=None) == NULL and Q(ke=None) == NULL and A(v=None) == NULL and A(ke=None) == NULL
+    assert Q(q8=MIS) == ALIGN and Q(qe=ctypes.c_void_p(4098)) == ALIGN and A(o=MIS) == ALIGN and A(ke=ctypes.c_void_p(4097)) == ALIGN
+    assert A(ws=None) == WORKSPACE and A(wsb=1) == WORKSPACE
+    assert Q(rows=0, q=None, k=None) == OK and A(n_seg=0, v=None) == OK and A(rows=0, o=None) == OK

@@ -683,3 +683,15 @@ def test_fp8qk_attention_error_against_exact_attention():
     want = oracle.attention(q.astype(np.float32).astype(np.float64), k.astype(np.float32).astype(np.float64), v, cu)
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     assert 1e-4 < rel < 5e-2
+
+
+def test_attention_base2_rows_is_the_restriction():
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((200, 3, 16)) for _ in range(3))
+    cu = np.array([0, 70, 70, 200])
+    full = oracle.attention_base2(q, k, v, cu)
+    rows = [0, 5, 69, 70, 150, 199]
+    assert np.allclose(oracle.attention_base2_rows(q, k, v, cu, rows, heads=[2, 0]), full[rows][:, [2, 0]],
+                       atol=1e-14, rtol=0)
+    # base-2 logits are natural logits times ln 2
+    assert np.allclose(full, oracle.attention(q, k, v, cu, softmax_scale=math.log(2.0)), atol=1e-12, rtol=0)
