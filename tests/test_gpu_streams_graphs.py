@@ -123,3 +123,78 @@ def test_step_captured_in_a_hip_graph_replays_exactly():
         g.replay()
         torch.cuda.synchronize()
         assert _same(S.results(), ref2)
+
+
+def _fp8_and_vsa_buffers(seed):
+    lengths, H = [700, 65, 1300], 3
+    rows = sum(lengths)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q, k, v = ((torch.randn((rows, H, 128), generator=g) * 0.5).to(torch.bfloat16).cuda() for _ in range(3))
+    cu = torch.tensor([0, 700, 765, rows], dtype=torch.int32, device="cuda")
+    b = dict(q=q, k=k, v=v, cu=cu, rows=rows, H=H, max_len=max(lengths), topk=5)
+    b["q8"] = torch.empty((rows, H, 128), dtype=torch.uint8, device="cuda")
+    b["k8"] = torch.empty_like(b["q8"])
+    b["qe"] = torch.empty((rows, H, 4), dtype=torch.uint8, device="cuda")
+    b["ke"] = torch.empty_like(b["qe"])
+    b["o8"] = torch.empty_like(v)
+    b["ws"] = h3.workspace(h3.attn_workspace_bytes(rows, 3), "cuda")
+    nb = h3.vsa_blocks_bound(rows, 3)
+    b["sel"] = torch.full((H, nb, 5), -1, dtype=torch.int32, device="cuda")
+    b["ov"] = torch.empty_like(v)
+    b["wsv"] = h3.workspace(h3.load().h3_vsa_workspace_bytes(rows, 3, H), "cuda")
+    return b
+
+
+def _fp8_and_vsa_run(b):
+    h3.quantize_qk_fp8(b["q"], b["k"], b["rows"], q8=b["q8"], qe=b["qe"], k8=b["k8"], ke=b["ke"])
+    h3.varlen_attn_fwd_fp8qk(b["q8"], b["qe"], b["k8"], b["ke"], b["v"], b["cu"], b["rows"], b["max_len"],
+                             o=b["o8"], ws=b["ws"])
+    h3.vsa_select(b["q"], b["k"], b["cu"], b["rows"], b["topk"], max_seqlen=b["max_len"], sel=b["sel"], ws=b["wsv"])
+    h3.vsa_attn_fwd(b["q"], b["k"], b["v"], b["cu"], b["rows"], b["sel"], b["topk"], o=b["ov"], ws=b["wsv"])
+
+
+def _fp8_and_vsa_results(b):
+    return [b[n].clone() for n in ("q8", "qe", "k8", "ke", "o8", "sel", "ov")]
+
+
+def _fp8_and_vsa_clear(b):
+    for n in ("q8", "qe", "k8", "ke"):
+        b[n].fill_(0x55)
+    b["sel"].fill_(-1)
+    b["o8"].fill_(float("nan"))
+    b["ov"].fill_(float("nan"))
+
+
+def test_fp8_and_vsa_calls_captured_in_a_hip_graph():
+    b = _fp8_and_vsa_buffers(31)
+    _fp8_and_vsa_run(b)
+    torch.cuda.synchronize()
+    ref = _fp8_and_vsa_results(b)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _fp8_and_vsa_run(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _fp8_and_vsa_run(b)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        _fp8_and_vsa_clear(b)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(_fp8_and_vsa_results(b), ref)
+    b["k"].mul_(-0.5)                      # new inputs in place: replays recompute
+    _fp8_and_vsa_clear(b)
+    _fp8_and_vsa_run(b)
+    torch.cuda.synchronize()
+    ref2 = _fp8_and_vsa_results(b)
+    assert not torch.equal(ref2[4], ref[4])
+    _fp8_and_vsa_clear(b)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert _same(_fp8_and_vsa_results(b), ref2)
