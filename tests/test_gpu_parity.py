@@ -69,6 +69,20 @@ def test_ragged_segments(D, dtype):
     _check_full(wl, g, r)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_many_short_segments(D):
+    # thousands of segments of 0..12 rows: one query tile each, the segment
+    # search over a long prefix, pack counts spread over many (segment, block)
+    # cells, empty segments between non-empty ones
+    rng = np.random.default_rng(21)
+    lengths = [int(x) for x in rng.integers(0, 13, size=3000)]
+    wl = W.make_custom(lengths, H=2, D=D, time_offset=3.0)
+    q, k, v = W.make_qkv(wl, seed=78)
+    g = run_path(wl, device_inputs(wl, q, k, v))
+    r = _oracle_full(wl, q, k, v)
+    _check_full(wl, g, r)
+
+
 def test_medium_8527_tokens_full():
     wl = W.make_workload(1)
     q, k, v = W.make_qkv(wl)
