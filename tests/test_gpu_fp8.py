@@ -121,3 +121,31 @@ def test_fp8_attention_accuracy_against_exact_attention():
     # 3 mantissa bits: ~1 % relative RMS on these N(0, 0.25) rows; a wrong
     # scale or exponent base would be off by orders of magnitude
     assert 1e-3 < rel < 3e-2, rel
+
+
+@pytest.mark.parametrize("rate", [0.3, 0.04])
+def test_fp8_attention_rescales_along_the_sequence(rate):
+    """Logits that climb along each segment by `rate` (log2 units) per key, so
+    the reference max moves every one (0.3) or every few (0.04) 32-key halves
+    deep inside the main loop, including on consecutive halves: the kernel
+    scales O one step after it finds the move (P.V runs one half behind the
+    exponentials).  Every row checked against the oracle on the dequantized
+    operands."""
+    lengths, H = [3000, 1500, 200], 2
+    rows = sum(lengths)
+    q, k, v = _packed(rows, H, seed=45)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    amp = 4.0
+    qf, kf = q.float() * 0.1, k.float() * 0.1
+    qf[:, :, 0] += amp
+    ramp = rate / (128 ** -0.5 * np.log2(np.e) * amp)
+    for a, b in zip(cu[:-1], cu[1:]):
+        kf[a:b, :, 0] += (torch.arange(b - a, dtype=torch.float32) * ramp)[:, None]
+    q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+    q8, qe, k8, ke = h3.quantize_qk_fp8(q.cuda(), k.cuda(), rows)
+    o = h3.varlen_attn_fwd_fp8qk(q8, qe, k8, ke, v.cuda(), torch.from_numpy(cu).cuda(), rows, max(lengths))
+    torch.cuda.synchronize()
+    qc, qx, kc, kx = _check_codes((q8, qe, k8, ke), q, k, rows)
+    ref = oracle.attention_base2(oracle.dequantize_mx_e4m3(qc, qx), oracle.dequantize_mx_e4m3(kc, kx),
+                                 _f32(v).astype(np.float64), cu)
+    assert_close(o[:rows], ref, "bf16", "fp8 O rescale rate %g" % rate)
