@@ -50,5 +50,61 @@ __device__ __forceinline__ int find_segment(const int32_t* __restrict__ prefix, 
 template <int N>
 struct Int { static constexpr int value = N; };
 
+// Largest of a lane's 16 scores of one 32-key half.
+__device__ __forceinline__ float lane_max16(const f32x16_t& s) {
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  return mx;
+}
+
+// P = exp2(S) for one 32-key half (S already relative to the reference), as
+// the two bf16 B operands of the P.V product; l gains the row sum of that
+// bf16 P (v_dot2c_f32_bf16 against ones), the P the product actually uses.
+__device__ __forceinline__ void exp2_to_bf16(const f32x16_t& sacc, bf16x8_t (&pk)[2], float& l_run) {
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = l_run;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+    }
+  }
+  l_run = lsum;
+}
+
+// Byte offsets, within a swizzled 64-key V tile, of the lane's transposing
+// reads: ds_read_b64_tr_b16 at voff[db] (+ 8 rows for the second half of the
+// operand) yields the V^T A operand of output block db (d = 32db .. +31).
+__device__ __forceinline__ void v_tr_offsets(int lane, int (&voff)[4]) {
+  const int g = lane >> 5;
+  const int rl = 4 * g + ((lane & 15) >> 2);
+  const int sv = swz_v(rl);
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
+}
+
+// O^T += V^T P^T for the 32 keys of one half whose V rows start at vh_l (two
+// transposing reads per V^T operand).
+__device__ __forceinline__ void pv_half_tr(const char* vh_l, const int (&voff)[4], const bf16x8_t (&pk)[2],
+                                           f32x16_t (&oacc)[4]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const char* vp = vh_l + voff[db] + (16 * c) * 256;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
+    }
+}
+
 }  // namespace
 }  // namespace h3

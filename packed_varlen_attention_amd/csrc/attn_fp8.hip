@@ -250,21 +250,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
 #pragma unroll
     for (int c = 0; c < 2; ++c) koff[m][c] = r32 * 128 + (((4 * m + 2 * c + g) ^ swz_k8(r32)) << 4);
   int voff[4];
-  {
-    const int rl = 4 * g + ((lane & 15) >> 2);
-    const int sv = swz_v(rl);
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
-  }
+  v_tr_offsets(lane, voff);
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
   float m_run = 0.f, l_run = 0.f;
   f32x16_t neg_m = f32x16_t{};
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // S^T for one 32-key half: two scaled fp8 instructions
   auto compute_s = [&](int stage, int half, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
@@ -290,15 +282,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
       }
     }
   };
-  auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
-    float mx = sacc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    return mx;
-  };
   // rare: a half tile's scores exceed the reference by more than 2^8
   auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
-    const float mloc = lane_max(sacc);
+    const float mloc = lane_max16(sacc);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
       __asm__ volatile("; rescale" ::: "memory");
       const float mpair = swap_halves_max(mloc);
@@ -315,32 +301,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
       }
     }
   };
-  auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-    float lsum = l_run;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-      }
-    }
-    l_run = lsum;
-  };
   auto pv_half = [&](int stage, int half, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-    const char* vh_l = v_stage(stage) + half * 8192;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const char* vp = vh_l + voff[db] + (16 * c) * 256;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
-      }
+    pv_half_tr(v_stage(stage) + half * 8192, voff, pk, oacc);
   };
 
   // ---- prologue: first half of tile 0 sets the reference
@@ -349,7 +311,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
   __syncthreads();
   compute_s(0, 0, scur, false);
   mask_tail(scur, 0);
-  m_run = swap_halves_max(lane_max(scur));
+  m_run = swap_halves_max(lane_max16(scur));
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     scur[i] -= m_run;
@@ -360,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
       __attribute__((always_inline)) {
     bf16x8_t pk[2];
     f32x16_t snxt;
-    exp_half(scur, pk);
+    exp2_to_bf16(scur, pk, l_run);
     compute_s(k_st, k_half, snxt, true);
     pv_half(v_st, v_half, pk);
     if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
@@ -369,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
   };
   auto final_step = [&](int v_st, int v_half) __attribute__((always_inline)) {
     bf16x8_t pk[2];
-    exp_half(scur, pk);
+    exp2_to_bf16(scur, pk, l_run);
     pv_half(v_st, v_half, pk);
   };
   auto tile = [&](auto phase, int j, auto steady) __attribute__((always_inline)) {

@@ -391,21 +391,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
   int voff[4];
-  {
-    const int rl = 4 * g + ((lane & 15) >> 2);
-    const int sv = swz_v(rl);
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
-  }
+  v_tr_offsets(lane, voff);
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
   float m_run = 0.f, l_run = 0.f;   // reference max (log2 units), row sum
   f32x16_t neg_m = f32x16_t{};      // -m_run in all 16 elements: S accumulator input
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // S^T for one 32-key half (16 fp32 per lane, all of the lane's query),
   // minus m when `biased`
@@ -428,17 +420,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
       }
     }
   };
-  auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
-    float mx = sacc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    return mx;
-  };
   // Rare path: a half tile's scores exceed the reference by more than 2^8.
   // Move m to the pair's max, rescale O and l by 2^-delta, and shift the
   // pending scores (computed against the old m) by -delta.
   auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
-    const float mloc = lane_max(sacc);
+    const float mloc = lane_max16(sacc);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
       // The empty volatile asm keeps the compiler from if-converting this
       // into an unconditional rescale on every step.
@@ -472,35 +458,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
       }
     }
   };
-  // P = exp2(S - m) as bf16 B operands, row sums accumulated
-  auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-    float lsum = l_run;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-      }
-    }
-    l_run = lsum;
-  };
-  // O^T += V^T P^T for the 32 keys of one half (two transpose reads per
-  // V^T operand)
-  auto pv_half = [&](const char* vh_l, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const char* vp = vh_l + voff[db] + (16 * c) * 256;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
-      }
-  };
   auto k_half = [&](int stage, int half) __attribute__((always_inline)) { return k_stage(stage) + half * 8192; };
   auto v_half = [&](int stage, int half) __attribute__((always_inline)) { return v_stage(stage) + half * 8192; };
 
@@ -511,7 +468,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
   __syncthreads();
   compute_s(k_half(0, 0), scur, false);
   mask_tail(scur, 0);
-  m_run = swap_halves_max(lane_max(scur));
+  m_run = swap_halves_max(lane_max16(scur));
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     scur[i] -= m_run;
@@ -526,17 +483,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
   auto step = [&](const char* k_next, int key_next, const char* v_cur, auto ragged) __attribute__((always_inline)) {
     bf16x8_t pk[2];
     f32x16_t snxt;
-    exp_half(scur, pk);
+    exp2_to_bf16(scur, pk, l_run);
     compute_s(k_next, snxt, true);
-    pv_half(v_cur, pk);
+    pv_half_tr(v_cur, voff, pk, oacc);
     if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
     update_max(snxt);
     scur = snxt;
   };
   auto final_step = [&](const char* v_cur) __attribute__((always_inline)) {
     bf16x8_t pk[2];
-    exp_half(scur, pk);
-    pv_half(v_cur, pk);
+    exp2_to_bf16(scur, pk, l_run);
+    pv_half_tr(v_cur, voff, pk, oacc);
   };
   // Tile j lives in stage j % kStages: its second half, then (after the
   // barrier that frees tile j-1's stage for tile j+kStages-1) the next tile's

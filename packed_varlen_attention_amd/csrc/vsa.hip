@@ -515,21 +515,13 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
   int voff[4];
-  {
-    const int rl = 4 * g + ((lane & 15) >> 2);
-    const int sv = swz_v(rl);
-    const int cl4 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl4 ^ (sv & 3))) << 4) + (lane & 1) * 8;
-  }
+  v_tr_offsets(lane, voff);
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
   float m_run = 0.f, l_run = 0.f;
   f32x16_t neg_m = f32x16_t{};
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   auto compute_s = [&](const char* kl, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
 #pragma unroll
@@ -548,45 +540,13 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
       }
     }
   };
-  auto lane_max = [&](const f32x16_t& sacc) __attribute__((always_inline)) {
-    float mx = sacc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-    return mx;
-  };
-  auto exp_half = [&](const f32x16_t& sacc, bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-    float lsum = l_run;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pk[c][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[c * 8 + e]);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2_t pp = {pk[c][e], pk[c][e + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-      }
-    }
-    l_run = lsum;
-  };
-  auto pv_half = [&](const char* vl, const bf16x8_t (&pk)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const char* vp = vl + voff[db] + (16 * c) * 256;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
-      }
-  };
   bool first = true;
   // one 32-key half: S, reference / rescale test, P, O += V P
   auto half_step = [&](const char* kl, const char* vl, int key_rel) __attribute__((always_inline)) {
     f32x16_t sacc;
     compute_s(kl, sacc, !first);
     mask_tail(sacc, key_rel);
-    const float mloc = lane_max(sacc);
+    const float mloc = lane_max16(sacc);
     if (first) {
       // the first half of the first kept block sets the reference
       m_run = swap_halves_max(mloc);
@@ -612,8 +572,8 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
       }
     }
     bf16x8_t pk[2];
-    exp_half(sacc, pk);
-    pv_half(vl, pk);
+    exp2_to_bf16(sacc, pk, l_run);
+    pv_half_tr(vl, voff, pk, oacc);
   };
   // Barrier without the workgroup fence of __syncthreads, which would wait
   // for every tile load in flight: this wave's LDS reads complete first; the
