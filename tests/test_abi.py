@@ -231,3 +231,27 @@ def test_fp8qk_host_validation(lib):
     assert Q(q8=MIS) == ALIGN and Q(qe=ctypes.c_void_p(4098)) == ALIGN and A(o=MIS) == ALIGN and A(ke=ctypes.c_void_p(4097)) == ALIGN
     assert A(ws=None) == WORKSPACE and A(wsb=1) == WORKSPACE
     assert Q(rows=0, q=None, k=None) == OK and A(n_seg=0, v=None) == OK and A(rows=0, o=None) == OK
+
+
+def test_fp8_binding_checks_before_any_call():
+    """The binding rejects inconsistent tensors itself, before a library call
+    (CPU tensors here are never passed to a kernel)."""
+    import torch
+    q = torch.zeros((10, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        h3.quantize_qk_fp8(q, torch.zeros((10, 3, 128), dtype=torch.bfloat16), 10)     # K heads differ
+    with pytest.raises(ValueError):
+        h3.quantize_qk_fp8(q, q, 11)                                                    # rows past the tensors
+    with pytest.raises(TypeError):
+        h3.quantize_qk_fp8(q, q, 10, q8=torch.zeros((10, 2, 128), dtype=torch.int8))  # codes must be uint8
+    with pytest.raises(ValueError):
+        h3.quantize_qk_fp8(q, q, 10, qe=torch.zeros((9, 2, 4), dtype=torch.uint8))   # exponents too small
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        h3.varlen_attn_fwd_fp8qk(u8(10, 2, 128), u8(10, 2, 4), u8(10, 2, 128), u8(10, 2, 4), q,
+                                 cu.to(torch.int64), 10)
+    with pytest.raises(ValueError):
+        h3.varlen_attn_fwd_fp8qk(u8(10, 2, 128), u8(10, 2, 4), u8(10, 2, 128), u8(10, 2, 4), q, cu, 11)
+    with pytest.raises(ValueError):
+        h3.varlen_attn_fwd_fp8qk(u8(10, 2, 128), u8(10, 2, 2), u8(10, 2, 128), u8(10, 2, 4), q, cu, 10)
