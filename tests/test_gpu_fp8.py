@@ -149,3 +149,22 @@ def test_fp8_attention_rescales_along_the_sequence(rate):
     ref = oracle.attention_base2(oracle.dequantize_mx_e4m3(qc, qx), oracle.dequantize_mx_e4m3(kc, kx),
                                  _f32(v).astype(np.float64), cu)
     assert_close(o[:rows], ref, "bf16", "fp8 O rescale rate %g" % rate)
+
+
+def test_fp8_and_vsa_attention_repeat_bit_identical():
+    """Both kernels order their work by item index only (the VSA kernel's
+    rotated key-block walk included), so repeated calls give identical bits."""
+    lengths, H = [1300, 700, 65], 3
+    rows = sum(lengths)
+    q, k, v = (t.cuda() for t in _packed(rows, H, seed=46))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).cuda()
+    q8, qe, k8, ke = h3.quantize_qk_fp8(q, k, rows)
+    sel = h3.vsa_select(q, k, cu, rows, 7, max_seqlen=max(lengths))
+    runs = []
+    for _ in range(3):
+        a = h3.varlen_attn_fwd_fp8qk(q8, qe, k8, ke, v, cu, rows, max(lengths))
+        b = h3.vsa_attn_fwd(q, k, v, cu, rows, sel, 7)
+        torch.cuda.synchronize()
+        runs.append((a.clone(), b.clone()))
+    for a, b in runs[1:]:
+        assert torch.equal(a, runs[0][0]) and torch.equal(b, runs[0][1])
