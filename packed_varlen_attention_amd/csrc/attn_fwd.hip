@@ -483,6 +483,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
   auto step = [&](const char* k_next, int key_next, const char* v_cur, auto ragged) __attribute__((always_inline)) {
     bf16x8_t pk[2];
     f32x16_t snxt;
+    // Scheduling hint: interleave the step's LDS reads with its MFMAs in
+    // small groups (measured 0.5 % faster at the 58,758-token step, same bits).
+    __builtin_amdgcn_iglp_opt(0);
     exp2_to_bf16(scur, pk, l_run);
     compute_s(k_next, snxt, true);
     pv_half_tr(v_cur, voff, pk, oacc);
