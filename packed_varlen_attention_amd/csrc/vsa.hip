@@ -543,6 +543,9 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   bool first = true;
   // one 32-key half: S, reference / rescale test, P, O += V P
   auto half_step = [&](const char* kl, const char* vl, int key_rel) __attribute__((always_inline)) {
+    // scheduling hint: LDS reads interleaved with the MFMAs in small groups
+    // (measured 1 % faster, same bits)
+    __builtin_amdgcn_iglp_opt(0);
     f32x16_t sacc;
     compute_s(kl, sacc, !first);
     mask_tail(sacc, key_rel);
