@@ -154,7 +154,8 @@ h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
  * or x = K: e = the smallest integer with max|x| <= 448 * 2^e (-127 for an
  * all-zero block, clamped to [-127, 127]), exponent byte e + 127, and each
  * code the E4M3 value nearest to x * 2^-e, ties to even mantissa, sign bit
- * from x.  softmax_scale 0 means 1/sqrt(D).
+ * from x.  softmax_scale 0 means 1/sqrt(D).  Q and K must be finite (an infinite or
+ * NaN element makes its block's exponent and codes meaningless).
  *
  *   q, k     : packed bf16 [>= rows][H][128] (device, 16-byte aligned)
  *   q8, k8   : uint8 codes [rows][H][128] out (16-byte aligned)
