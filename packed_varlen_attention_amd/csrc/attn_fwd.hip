@@ -585,6 +585,329 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short-segment variant of the D = 128 kernel (segments of at most
+// kShortMaxLen rows, as in 3-D window attention): 4 waves x 32 query rows =
+// 128 rows per workgroup, 32-key K/V tiles in a 4-stage ring of 64 KB, so two
+// workgroups share a CU and one's prologue (Q and first tiles) and epilogue
+// (O store) overlap the other's matrix work.  Per query row the arithmetic is
+// the main kernel's, step for step (32-key halves in key order, the same
+// reference and rescale points), so the two give identical bits.
+// ---------------------------------------------------------------------------
+constexpr int kBMs = 128;                 // query rows per workgroup
+constexpr int kShortMaxLen = 512;         // longest segment routed to it
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_short_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    int n_seg, int H, int total_rows, float scale_log2) {
+  constexpr int D = 128;
+  constexpr int NW = 4;                    // waves per workgroup
+  constexpr int DMA_ROWS = 32 / NW;        // tile rows each wave loads per tensor
+  constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
+  constexpr int kB = kTileBytes / 2;       // one 32-key K or V tile
+  __shared__ __attribute__((aligned(1024))) char lk0[kB], lk1[kB], lk2[kB], lk3[kB];
+  __shared__ __attribute__((aligned(1024))) char lv0[kB], lv1[kB], lv2[kB], lv3[kB];
+  // stage is a compile-time constant at every call, so these fold away
+  auto k_stage = [&](int stage) __attribute__((always_inline)) -> char* {
+    return stage == 0 ? lk0 : stage == 1 ? lk1 : stage == 2 ? lk2 : lk3;
+  };
+  auto v_stage = [&](int stage) __attribute__((always_inline)) -> char* {
+    return stage == 0 ? lv0 : stage == 1 ? lv1 : stage == 2 ? lv2 : lv3;
+  };
+
+  // ---- work item (same XCD-aware head-major order as the generic kernel)
+  const int T = prefix[n_seg];
+  const int64_t W = (int64_t)T * H;
+  const int64_t per = (W + 7) >> 3;
+  const int64_t jj = blockIdx.x >> 3;
+  const int64_t w = (int64_t)(blockIdx.x & 7) * per + jj;
+  if (jj >= per || w >= W) return;
+  const int h = (int)(w / T), t = (int)(w - (int64_t)h * T);
+  const int s = find_segment(prefix, n_seg, t);
+  const int seg_start = min(max(cu[s], 0), total_rows);
+  const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+  const int L = seg_end - seg_start;
+  const int q0 = seg_start + (t - prefix[s]) * kBMs;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
+  const int g = lane >> 5, r32 = lane & 31;
+  const int64_t rs = (int64_t)H * D;
+
+  // ---- direct HBM -> LDS tile loads: wave w fills tile rows
+  // DMA_ROWS*w .. +DMA_ROWS-1, four rows (1 KB) per instruction; lane i
+  // writes LDS slot i, so it fetches the chunk that the swizzle places there.
+  // Byte offsets are relative to the tile's first row (< 64 rows * H*D*2 B,
+  // which the host keeps below 2^31).
+  const uint16_t* kseg = k + (int64_t)seg_start * rs + (int64_t)h * D;
+  const uint16_t* vseg = v + (int64_t)seg_start * rs + (int64_t)h * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  int drow[DMA_INSTR], kch[DMA_INSTR], vch[DMA_INSTR];
+  uint32_t koff_dma[DMA_INSTR], voff_dma[DMA_INSTR];
+#pragma unroll
+  for (int tt = 0; tt < DMA_INSTR; ++tt) {
+    drow[tt] = DMA_ROWS * wave + 4 * tt + (lane >> 4);
+    kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
+    vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
+    koff_dma[tt] = (uint32_t)drow[tt] * row_bytes + (uint32_t)kch[tt] * 16u;
+    voff_dma[tt] = (uint32_t)drow[tt] * row_bytes + (uint32_t)vch[tt] * 16u;
+  }
+  auto issue_tile = [&](int tile_rel, int stage) __attribute__((always_inline)) {
+    char* kb_l = k_stage(stage);
+    char* vb_l = v_stage(stage);
+    const int nrec = (int)(32u * row_bytes);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kseg + (int64_t)tile_rel * rs), (short)0, nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vseg + (int64_t)tile_rel * rs), (short)0, nrec, kBufferWord3);
+    if (__builtin_expect(tile_rel + 32 <= L, 1)) {
+#pragma unroll
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 koff_dma[tt], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 voff_dma[tt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < DMA_INSTR; ++tt) {
+        const uint32_t row = (uint32_t)min(drow[tt], L - 1 - tile_rel);   // ragged tail: repeat the last row
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + (uint32_t)kch[tt] * 16u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vb_l + (DMA_ROWS * wave + 4 * tt) * 256), 16,
+                                                 row * row_bytes + (uint32_t)vch[tt] * 16u, 0, 0, 0);
+      }
+    }
+  };
+
+  // s_waitcnt vmcnt(n * loads per tile): all but the newest n tiles landed
+  auto wait_tiles_in_flight = [&](int n) __attribute__((always_inline)) {
+    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * DMA_INSTR));
+  };
+  static_assert(kStages == 4 && 4 * DMA_INSTR <= 15, "vmcnt encoding above assumes <= 15 loads in flight");
+  const int ntiles = (L + 31) >> 5;
+#pragma unroll
+  for (int t0 = 0; t0 < kStages - 1; ++t0)
+    if (t0 < ntiles) issue_tile(t0 * 32, t0);
+
+  // ---- Q fragment (B operand), times scale * log2(e): lane holds
+  // Q[row r32][d = 16kc + 8g .. +8]
+  bf16x8_t qf[8];
+  {
+    const int qrow = q0 + wave * 32 + r32;
+    if (qrow < seg_end) {
+      const uint16_t* qp = q + qrow * rs + (int64_t)h * D + g * 8;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        qf[kc] = *reinterpret_cast<const bf16x8_t*>(qp + kc * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[kc][e] = (__bf16)((float)qf[kc][e] * scale_log2);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) qf[kc] = bf16x8_t{};
+    }
+  }
+
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
+  int voff[4];
+  v_tr_offsets(lane, voff);
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+  float m_run = 0.f, l_run = 0.f;   // reference max (log2 units), row sum
+  f32x16_t neg_m = f32x16_t{};      // -m_run in all 16 elements: S accumulator input
+
+  // S^T for one 32-key half (16 fp32 per lane, all of the lane's query),
+  // minus m when `biased`
+  auto compute_s = [&](const char* kh_l, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kh_l + koff[kc]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
+                                                     0, 0, 0);
+    }
+  };
+  // keys past the segment end get -inf (only a segment's last, ragged tile)
+  auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
+    if (__builtin_expect(key_rel + 32 > L, 0)) {
+      __asm__ volatile("; ragged tail" ::: "memory");   // keep it a branch, not selects
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= L) sacc[i] = -INFINITY;
+      }
+    }
+  };
+  // Rare path: a half tile's scores exceed the reference by more than 2^8.
+  // Move m to the pair's max, rescale O and l by 2^-delta, and shift the
+  // pending scores (computed against the old m) by -delta.
+  auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
+    const float mloc = lane_max16(sacc);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
+      // The empty volatile asm keeps the compiler from if-converting this
+      // into an unconditional rescale on every step.
+      __asm__ volatile("; rescale" ::: "memory");
+      const float mpair = swap_halves_max(mloc);
+      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+      float alpha = __builtin_amdgcn_exp2f(-delta);
+      // The multiplies below are inline asm, which the compiler's hazard
+      // checks do not see: wait out the v_exp_f32 result (transcendental
+      // write -> VALU read) and the last PV MFMA writes of oacc (matrix
+      // result -> VALU read/write) here.  Routing alpha through the asm pins
+      // the exp before the wait.
+      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
+      l_run *= alpha;
+      // In-place multiply: the accumulators keep their registers on both
+      // sides of this branch, so the common path pays no register copies.
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = oacc[db][i];
+          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+          oacc[db][i] = x;
+        }
+      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
+      m_run += delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] -= delta;
+        neg_m[i] = -m_run;
+      }
+    }
+  };
+
+  // ---- prologue: first half of tile 0; its max sets the reference
+  f32x16_t scur;
+  // tile 0 must have landed; tiles 1 .. kStages-2 may still be in flight
+  wait_tiles_in_flight(min(ntiles - 1, kStages - 2));
+  __syncthreads();
+  compute_s(k_stage(0), scur, false);
+  mask_tail(scur, 0);
+  m_run = swap_halves_max(lane_max16(scur));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    scur[i] -= m_run;
+    neg_m[i] = -m_run;
+  }
+
+  // One pipeline step: S of the next half on the matrix cores while the
+  // vector ALU exponentiates the current half, then O += V P for the current
+  // half while the next half's scores are checked against the reference.
+  // `ragged` is false where the next half cannot reach past the segment end
+  // (the main loop): no test there keeps the step one basic block.
+  auto step = [&](const char* k_next, int key_next, const char* v_cur, auto ragged) __attribute__((always_inline)) {
+    bf16x8_t pk[2];
+    f32x16_t snxt;
+    // Scheduling hint: interleave the step's LDS reads with its MFMAs in
+    // small groups (measured 0.5 % faster at the 58,758-token step, same bits).
+    __builtin_amdgcn_iglp_opt(0);
+    exp2_to_bf16(scur, pk, l_run);
+    compute_s(k_next, snxt, true);
+    pv_half_tr(v_cur, voff, pk, oacc);
+    if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
+    update_max(snxt);
+    scur = snxt;
+  };
+  auto final_step = [&](const char* v_cur) __attribute__((always_inline)) {
+    bf16x8_t pk[2];
+    exp2_to_bf16(scur, pk, l_run);
+    pv_half_tr(v_cur, voff, pk, oacc);
+  };
+  // Tile j (32 keys) lives in stage j % kStages: after the barrier that
+  // frees tile j-1's stage for tile j+kStages-1, the step that exponentiates
+  // tile j's scores, computes tile j+1's and adds V P of tile j.  `steady`:
+  // tile j+1 exists and is not the last one, so no exit paths or tail mask.
+  auto tile = [&](auto phase, int j, auto steady) __attribute__((always_inline)) {
+    constexpr int cur = decltype(phase)::value;
+    constexpr int nxt = (cur + 1) % kStages;
+    constexpr int dma = (cur + kStages - 1) % kStages;
+    constexpr bool is_steady = decltype(steady)::value != 0;
+    if (is_steady || j + 1 < ntiles) {
+      // tile j+1 must have landed; younger tiles may still be in flight
+      wait_tiles_in_flight(min(ntiles - 2 - j, kStages - 3));
+      __syncthreads();
+      if (j + kStages - 1 < ntiles) issue_tile((j + kStages - 1) * 32, dma);
+      step(k_stage(nxt), (j + 1) * 32, v_stage(cur), Int<is_steady ? 0 : 1>{});
+    } else {
+      final_step(v_stage(cur));
+    }
+  };
+
+  // Main loop: kStages tiles per trip, one back-edge, so the accumulators
+  // keep their registers across the unrolled copies.  A steady tile t also
+  // computes S for the first half of tile t+1 without the ragged-tail mask, so
+  // the loop stops while t+1 is still short of the last tile (t + 2 < ntiles).
+  // The last 1..kStages+1 tiles follow as straight-line code from stage 0.
+  int j = 0;
+  for (; j + kStages + 1 < ntiles; j += kStages) {
+    tile(Int<0>{}, j, Int<1>{});
+    tile(Int<1>{}, j + 1, Int<1>{});
+    tile(Int<2>{}, j + 2, Int<1>{});
+    tile(Int<3>{}, j + 3, Int<1>{});
+  }
+  tile(Int<0>{}, j, Int<0>{});
+  if (j + 1 < ntiles) {
+    tile(Int<1>{}, j + 1, Int<0>{});
+    if (j + 2 < ntiles) {
+      tile(Int<2>{}, j + 2, Int<0>{});
+      if (j + 3 < ntiles) {
+        tile(Int<3>{}, j + 3, Int<0>{});
+        if (j + 4 < ntiles) tile(Int<0>{}, j + 4, Int<0>{});
+      }
+    }
+  }
+
+  // ---- normalise and store: lane holds O[row][d = 32db + 8a + 4g + 0..3].
+  // Each wave's 32 x 128 bf16 tile goes through LDS so that the global stores
+  // write whole rows (16 bytes per lane, 4 rows per instruction) instead of
+  // 16-byte pieces of 32 rows; on short segments, where the store sits on the
+  // critical path of every workgroup, this is ~10 % of the kernel.  Free LDS:
+  // every ring stage other than those of the last two tiles (all waves have
+  // passed the barrier after which nothing reads them, and every issued tile
+  // load has been waited for).
+  const float inv = 1.f / swap_halves_sum(l_run);
+  {
+    const int busy0 = (ntiles - 1) & 3, busy1 = ntiles >= 2 ? (ntiles - 2) & 3 : busy0;
+    int f0 = 0;
+    while (f0 == busy0 || f0 == busy1) ++f0;
+    int f1 = f0 + 1;
+    while (f1 == busy0 || f1 == busy1) ++f1;
+    const int fs = (wave >> 1) ? f1 : f0;
+    char* ot = (wave & 1) ? v_stage(fs) : k_stage(fs);   // 32 rows x 256 B, 16-byte chunks swizzled by row
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 st;
+        const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
+        const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
+        const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
+        const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
+        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        const int chunk = (4 * db + a4) ^ (r32 & 15);
+        *reinterpret_cast<uint2*>(ot + r32 * 256 + chunk * 16 + g * 8) = st;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's tile is in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4), c = lane & 15;
+      const uint4 x = *reinterpret_cast<const uint4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+      const int orow = q0 + wave * 32 + row;
+      if (orow < seg_end) *reinterpret_cast<uint4*>(o + orow * rs + (int64_t)h * D + c * 8) = x;
+    }
+  }
+}
+
 // Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
 // segment bounds clamped to [0, total_rows]; prefix[n_seg] = 0 before the scan.
 __global__ void tile_counts_kernel(const int32_t* __restrict__ cu, int n_seg, int total_rows, int bm,
@@ -620,9 +943,10 @@ hipError_t launch_build_tiles(const int32_t* cu, int n_seg, int total_rows, int 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
                             const int32_t* cu, int n_seg, int max_seqlen, int total_rows,
                             int H, int D, float scale, void* ws, hipStream_t stream) {
-  (void)max_seqlen;
   int32_t* prefix = static_cast<int32_t*>(ws);
-  const int bm = (D == 128) ? kBM2 : kBM;
+  // segments known to be short (host hint) go to the 2-workgroups-per-CU variant
+  const bool short_segs = D == 128 && max_seqlen > 0 && max_seqlen <= kShortMaxLen;
+  const int bm = (D == 128) ? (short_segs ? kBMs : kBM2) : kBM;
   hipError_t e = launch_build_tiles(cu, n_seg, total_rows, bm, prefix, stream);
   if (e != hipSuccess) return e;
   const int64_t t_max = ceil_div(total_rows, bm) + n_seg;
@@ -630,7 +954,11 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const int64_t grid = 8 * ceil_div(w_max, 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  if (D == 128)
+  if (short_segs)
+    attn_fwd_bf16_d128_short_kernel<<<(unsigned)grid, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
+  else if (D == 128)
     attn_fwd_bf16_d128_kernel<<<(unsigned)grid, 512, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
