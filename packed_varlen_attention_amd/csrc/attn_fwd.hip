@@ -908,6 +908,324 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_short_kernel(
   }
 }
 
+// Several-items-per-workgroup variant for short segments (the same
+// 128-row items as the short-segment kernel).  A fixed grid of two
+// workgroups per CU walks the XCD-aware item order with a stride, and the
+// 32-key K/V tiles of consecutive items flow through one 4-stage ring: the
+// tile loads run two tiles ahead of the consumer across item boundaries, and
+// the next item's Q is requested as soon as the current item's last scores
+// are computed (Q's registers are free from there), so one item's fixed costs
+// (Q and first tiles in flight, O normalised and stored) overlap another
+// item's matrix work instead of leaving the CU idle.  An item's first tile
+// sits in a ring stage set by the lengths of the items before it, so stages
+// are addressed at run time; the tile loads are issued as inline asm (the
+// compiler's wait-count pass does not see them, which keeps it from draining
+// every tile in flight at each barrier), every wait on them is an explicit
+// s_waitcnt, and the barriers are bare (lgkmcnt(0); s_barrier).  Per query
+// row the arithmetic is the main kernel's, step for step, so the output is
+// bit-identical to it.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMultiItemsPerSlot = 4;    // items per workgroup slot (host bound) that select it
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+    int n_seg, int H, int total_rows, float scale_log2) {
+  constexpr int D = 128;
+  constexpr int NW = 4;                    // waves per workgroup
+  constexpr int DMA_ROWS = 32 / NW;        // tile rows each wave loads per tensor
+  constexpr int DMA_INSTR = DMA_ROWS / 4;  // 4 rows (1 KB) per load instruction
+  constexpr int LOADS = 2 * DMA_INSTR;     // load instructions per tile per lane
+  constexpr int kB = kTileBytes / 2;       // one 32-key K or V tile (8 KB)
+  constexpr int NST = 4;                   // ring stages; stage s: K at 2s*kB, V at (2s+1)*kB
+  __shared__ __attribute__((aligned(1024))) char ring[NST * 2 * kB];
+
+  // ---- this workgroup's items: w = w_begin, w_begin + stride, ... < w_end
+  const int T = prefix[n_seg];             // items per head
+  const int W = T * H;                     // the host keeps the item count below 2^31
+  const int per = (W + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int stride = gridDim.x >> 3;
+  const int w_begin = xcd * per + (int)(blockIdx.x >> 3);
+  const int w_end = min(xcd * per + per, W);
+  if (w_begin >= w_end) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
+  const int g = lane >> 5, r32 = lane & 31;
+  const int64_t rs = (int64_t)H * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  // Item w: head, segment bounds (clamped as the tile counts were) and first query row.
+  struct Item { int h, seg_start, L, q0; };
+  auto item_at = [&](int w) __attribute__((always_inline)) -> Item {
+    Item it;
+    it.h = w / T;
+    const int t = w - it.h * T;
+    const int s = find_segment(prefix, n_seg, t);
+    it.seg_start = min(max(cu[s], 0), total_rows);
+    const int seg_end = max(min(cu[s + 1], total_rows), it.seg_start);
+    it.L = seg_end - it.seg_start;
+    it.q0 = it.seg_start + (t - prefix[s]) * kBMs;
+    return it;
+  };
+
+  // ---- tile loads (HBM -> LDS), as in the short-segment kernel: wave w
+  // fills tile rows DMA_ROWS*w .. +DMA_ROWS-1, lane i writes LDS slot i.
+  int drow[DMA_INSTR], kch[DMA_INSTR], vch[DMA_INSTR];
+#pragma unroll
+  for (int tt = 0; tt < DMA_INSTR; ++tt) {
+    drow[tt] = DMA_ROWS * wave + 4 * tt + (lane >> 4);
+    kch[tt] = (lane & 15) ^ swz_k(drow[tt]);
+    vch[tt] = (lane & 15) ^ swz_v(drow[tt]);
+  }
+  auto dma = [&](const u32x4_t& rsrc, const char* lds, uint32_t voffset) __attribute__((always_inline)) {
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0v), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  };
+  auto rsrc_of = [&](const uint16_t* base) __attribute__((always_inline)) -> u32x4_t {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                   32u * row_bytes, (uint32_t)kBufferWord3};
+  };
+  auto stage_k = [&](int gt) __attribute__((always_inline)) -> char* { return ring + (gt & (NST - 1)) * (2 * kB); };
+  auto stage_v = [&](int gt) __attribute__((always_inline)) -> char* { return stage_k(gt) + kB; };
+
+  // Issue cursor: the next tile to load is tile i_tile of item i_w, global tile number g_issue.
+  int i_w = w_begin, i_tile = 0, g_issue = 0;
+  Item i_it = item_at(i_w);
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if (i_w >= w_end) return;
+    const int key0 = i_tile * 32;
+    const uint16_t* kt = k + ((int64_t)i_it.seg_start + key0) * rs + (int64_t)i_it.h * D;
+    const uint16_t* vt = v + ((int64_t)i_it.seg_start + key0) * rs + (int64_t)i_it.h * D;
+    const u32x4_t rk = rsrc_of(kt), rv = rsrc_of(vt);
+    const char* kl = stage_k(g_issue);
+    const char* vl = stage_v(g_issue);
+    const int last = i_it.L - 1 - key0;    // last valid row of this tile, relative to its first
+#pragma unroll
+    for (int tt = 0; tt < DMA_INSTR; ++tt) {
+      const uint32_t row = (uint32_t)min(drow[tt], last);   // ragged tail: repeat the last row
+      dma(rk, kl + (DMA_ROWS * wave + 4 * tt) * 256, row * row_bytes + (uint32_t)kch[tt] * 16u);
+      dma(rv, vl + (DMA_ROWS * wave + 4 * tt) * 256, row * row_bytes + (uint32_t)vch[tt] * 16u);
+    }
+    ++g_issue;
+    if (++i_tile == (i_it.L + 31) >> 5) {
+      i_tile = 0;
+      i_w += stride;
+      if (i_w < w_end) i_it = item_at(i_w);
+    }
+  };
+  // s_waitcnt vmcnt: tile gt has landed.  Loads run two tiles ahead (before
+  // the scores of tile t, after the barrier, tile t+2 is requested into the
+  // stage of tile t-2, whose last reads came before that barrier), so at the
+  // wait at most tile gt+1 is younger; other memory operations issued after
+  // tile gt only make this wait longer, never shorter.
+  auto wait_tile = [&](int gt) __attribute__((always_inline)) {
+    if (g_issue - 1 - gt <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);
+  };
+  static_assert(LOADS <= 15, "vmcnt encoding above assumes <= 15 loads in flight");
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = r32 * 256 + (((2 * kc + g) ^ swz_k(r32)) << 4);
+  int voff[4];
+  v_tr_offsets(lane, voff);
+
+  // Q loads and O stores go through a buffer descriptor that ends at the
+  // item's last valid row: rows past the segment end read as zero and their
+  // stores are dropped by the range check, so every lane issues the same
+  // fixed number of each (kQLoads, kOStores) with no branch, and the waits
+  // below can count them.
+  constexpr int kOStores = 8;
+  auto rows_rsrc = [&](const uint16_t* base, const Item& it) __attribute__((always_inline)) {
+    const int nrows = min(it.seg_start + it.L - it.q0, kBMs);   // >= 1
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)it.q0 * rs + (int64_t)it.h * D),
+                                             (short)0, (int)((uint32_t)(nrows - 1) * row_bytes + 256u),
+                                             kBufferWord3);
+  };
+  bf16x8_t qf[8];
+  auto load_q = [&](const Item& it) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(q, it);
+    const uint32_t off = (uint32_t)(wave * 32 + r32) * row_bytes + (uint32_t)g * 16u;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+      qf[kc] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + kc * 32u), 0, 0));
+  };
+  auto scale_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kc][e] = (__bf16)((float)qf[kc][e] * scale_log2);
+  };
+
+  f32x16_t oacc[4];
+  float m_run, l_run;               // reference max (log2 units), row sum
+  f32x16_t neg_m;                   // -m_run in all 16 elements: S accumulator input
+  int L = 0;                        // current item's segment length
+
+  auto compute_s = [&](const char* kh_l, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kh_l + koff[kc]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
+                                                     0, 0, 0);
+    }
+  };
+  auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
+    if (__builtin_expect(key_rel + 32 > L, 0)) {
+      __asm__ volatile("; ragged tail" ::: "memory");   // keep it a branch, not selects
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key_rel + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= L) sacc[i] = -INFINITY;
+      }
+    }
+  };
+  // Rare path, as in the main kernel: move m by the pair's max when a half
+  // tile's scores exceed the reference by more than 2^8, rescale O and l.
+  auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
+    const float mloc = lane_max16(sacc);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
+      __asm__ volatile("; rescale" ::: "memory");
+      const float mpair = swap_halves_max(mloc);
+      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+      float alpha = __builtin_amdgcn_exp2f(-delta);
+      // wait states the hazard checks do not see through the asm multiplies
+      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = oacc[db][i];
+          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+          oacc[db][i] = x;
+        }
+      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
+      m_run += delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] -= delta;
+        neg_m[i] = -m_run;
+      }
+    }
+  };
+
+  // ---- prologue: the first two tiles, then the first item's Q
+#pragma unroll
+  for (int t0 = 0; t0 < NST - 2; ++t0) issue_next();
+  Item it = item_at(w_begin);
+  load_q(it);
+  scale_q();
+
+  int g_cons = 0;                   // global number of the current item's first tile
+  for (int w = w_begin;;) {
+    L = it.L;
+    const int nt = (L + 31) >> 5;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
+    l_run = 0.f;
+
+    // First tile: its max sets the reference.  The memory operations issued
+    // after this tile's loads are tile g_cons+1's loads, this item's Q loads
+    // and the previous item's kOStores O stores, in that order: keep the
+    // stores in flight, everything older has landed.
+    f32x16_t scur;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kOStores);
+    barrier();
+    issue_next();
+    compute_s(stage_k(g_cons), scur, false);
+    mask_tail(scur, 0);
+    m_run = swap_halves_max(lane_max16(scur));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      scur[i] -= m_run;
+      neg_m[i] = -m_run;
+    }
+    // S of tile r on the matrix cores while the vector ALU exponentiates
+    // tile r-1, then O += V P for tile r-1
+    for (int r = 1; r < nt; ++r) {
+      const int gt = g_cons + r;
+      wait_tile(gt);
+      barrier();
+      issue_next();
+      bf16x8_t pk[2];
+      f32x16_t snxt;
+      __builtin_amdgcn_iglp_opt(0);
+      exp2_to_bf16(scur, pk, l_run);
+      compute_s(stage_k(gt), snxt, true);
+      pv_half_tr(stage_v(gt - 1), voff, pk, oacc);
+      mask_tail(snxt, r * 32);
+      update_max(snxt);
+      scur = snxt;
+    }
+    // Q's registers are free: request the next item's rows now
+    const int w_next = w + stride;
+    Item nx = it;
+    if (w_next < w_end) {
+      nx = item_at(w_next);
+      load_q(nx);
+    }
+    const int g_last = g_cons + nt - 1;
+    {
+      bf16x8_t pk[2];
+      exp2_to_bf16(scur, pk, l_run);
+      pv_half_tr(stage_v(g_last), voff, pk, oacc);
+    }
+
+    // ---- normalise and store through LDS (whole 256-byte rows per store).
+    // The stages of tiles g_last-1 and g_last are free once every wave is
+    // past this barrier: the loads in flight are for tiles g_last+1 and
+    // g_last+2, and the next load (tile g_last+3, into g_last-1's stage)
+    // follows the next item's first barrier.
+    barrier();
+    const float inv = 1.f / swap_halves_sum(l_run);
+    {
+      const int gs = (wave >> 1) ? g_last : g_last - 1;
+      char* ot = (wave & 1) ? stage_v(gs) : stage_k(gs);   // 32 rows x 256 B, 16-byte chunks swizzled by row
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          uint2 st;
+          const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
+          const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
+          const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
+          const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
+          st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          const int chunk = (4 * db + a4) ^ (r32 & 15);
+          *reinterpret_cast<uint2*>(ot + r32 * 256 + chunk * 16 + g * 8) = st;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's tile is in LDS
+      const __amdgpu_buffer_rsrc_t ro = rows_rsrc(o, it);
+      static_assert(kOStores == 8, "one store per 4 rows of the wave's 32");
+#pragma unroll
+      for (int i = 0; i < kOStores; ++i) {
+        const int row = 4 * i + (lane >> 4), c = lane & 15;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(x, ro, (int)((uint32_t)(wave * 32 + row) * row_bytes + c * 16u), 0, 0);
+      }
+    }
+    g_cons += nt;
+    w = w_next;
+    if (w >= w_end) break;
+    it = nx;
+    scale_q();   // waits for the next item's Q only: the O stores above stay in flight
+  }
+  // every tile load was waited for (the cursor stops at the last item's last
+  // tile, which the last item consumed); LDS reads of the staging are done
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Tile counts per segment: prefix[s] = ceil(L_s / bm) (then scanned), with
 // segment bounds clamped to [0, total_rows]; prefix[n_seg] = 0 before the scan.
 __global__ void tile_counts_kernel(const int32_t* __restrict__ cu, int n_seg, int total_rows, int bm,
@@ -944,7 +1262,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             const int32_t* cu, int n_seg, int max_seqlen, int total_rows,
                             int H, int D, float scale, void* ws, hipStream_t stream) {
   int32_t* prefix = static_cast<int32_t*>(ws);
-  // segments known to be short (host hint) go to the 2-workgroups-per-CU variant
+  // segments known to be short (host hint) go to the 2-workgroups-per-CU variants
   const bool short_segs = D == 128 && max_seqlen > 0 && max_seqlen <= kShortMaxLen;
   const int bm = (D == 128) ? (short_segs ? kBMs : kBM2) : kBM;
   hipError_t e = launch_build_tiles(cu, n_seg, total_rows, bm, prefix, stream);
@@ -954,11 +1272,24 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const int64_t grid = 8 * ceil_div(w_max, 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  if (short_segs)
-    attn_fwd_bf16_d128_short_kernel<<<(unsigned)grid, 256, 0, stream>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-        static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
-  else if (D == 128)
+  if (short_segs) {
+    // Many items per workgroup slot: the several-items-per-workgroup variant,
+    // which overlaps one item's fixed costs with another's matrix work; with
+    // few, each workgroup takes one item.
+    int dev = 0, n_cu = 0;
+    hipError_t de = hipGetDevice(&dev);
+    if (de == hipSuccess) de = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (de != hipSuccess) return de;
+    const int64_t slots = 8 * ceil_div(2 * (int64_t)std::max(n_cu, 8), 8);   // two workgroups per CU
+    if (w_max >= kMultiItemsPerSlot * slots && w_max <= 0x7fffffff)
+      attn_fwd_bf16_d128_multi_kernel<<<(unsigned)slots, 256, 0, stream>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
+    else
+      attn_fwd_bf16_d128_short_kernel<<<(unsigned)grid, 256, 0, stream>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
+  } else if (D == 128)
     attn_fwd_bf16_d128_kernel<<<(unsigned)grid, 512, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);

@@ -323,3 +323,34 @@ def test_short_segment_kernel_matches_main_kernel_bit_for_bit():
     assert torch.equal(o_main[:wl.n], o_short[:wl.n])
     ref = oracle.attention(f64(q), f64(k), f64(v), cu)
     assert_close(o_short[:wl.n], ref, "bf16", "short-segment kernel")
+
+
+def test_multi_item_kernel_matches_main_kernel_bit_for_bit():
+    """With many short segments (at least four 128-row items per workgroup
+    slot), the short-segment call runs the several-items-per-workgroup
+    kernel: each workgroup walks a strided list of items, and the K/V tile
+    ring and the next item's Q loads run across item boundaries.  Ragged
+    tails, one-tile items, empty segments and planted rescales inside a
+    workgroup's item sequence; outputs identical to the main kernel's, and
+    to the oracle on two heads."""
+    base = [1, 31, 32, 33, 63, 64, 65, 0, 127, 128, 129, 255, 256, 257, 300, 511, 512]
+    lengths = [base[(7 * i) % len(base)] for i in range(8 * len(base))]
+    H = 24
+    wl = W.make_custom(lengths, H=H, D=128)
+    q, k, v = W.make_qkv(wl, seed=82)
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    qf, kf = q.float(), k.float()
+    qf[:, :, 0] += 3.0
+    kf[::37, :, 0] += 40.0
+    q, k = qf.to(q.dtype).cuda(), kf.to(k.dtype).cuda()
+    v = v.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    o_main = h3.varlen_attn_fwd(q, k, v, dcu, total_rows=wl.n, max_seqlen=0)
+    o_multi = h3.varlen_attn_fwd(q, k, v, dcu, total_rows=wl.n, max_seqlen=512)
+    o_again = h3.varlen_attn_fwd(q, k, v, dcu, total_rows=wl.n, max_seqlen=512)
+    torch.cuda.synchronize()
+    assert torch.equal(o_main[:wl.n], o_multi[:wl.n])
+    assert torch.equal(o_multi, o_again)
+    heads = [0, H - 1]
+    ref = oracle.attention(f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads]), cu)
+    assert_close(o_multi[:wl.n, heads], ref, "bf16", "several-items-per-workgroup kernel")
