@@ -302,8 +302,9 @@ def test_mfma_probe_runs_and_counts_flops():
 
 
 def test_short_segment_kernel_matches_main_kernel_bit_for_bit():
-    """Segments up to 512 rows with max_seqlen given go to the short-segment
-    kernel (128-row tiles, 32-key K/V tiles, two workgroups per CU); without
+    """Segments up to 512 rows with max_seqlen given, and few 128-row items
+    (here 147 for 512 workgroup slots), go to the short-segment kernel
+    (128-row tiles, 32-key K/V tiles, two workgroups per CU); without
     the hint the main kernel runs.  Per row both do the same arithmetic in the
     same order, so the outputs must be identical, and match the oracle."""
     lengths = [1, 31, 32, 33, 63, 64, 65, 0, 127, 128, 129, 255, 256, 257, 300, 511, 512]
