@@ -357,3 +357,20 @@ def test_multi_item_kernel_matches_main_kernel_bit_for_bit(H, repeats):
     heads = sorted({0, H - 1})
     ref = oracle.attention(f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads]), cu)
     assert_close(o_multi[:wl.n, heads], ref, "bf16", "several-items-per-workgroup kernel")
+
+
+@pytest.mark.parametrize("repeats", [1, 12])
+def test_max_seqlen_hint_below_a_segment_length_changes_nothing(repeats):
+    """The hint only selects kernels: with max_seqlen = 512 but segments of up
+    to 3,000 rows, the short-segment kernels (one item per workgroup for the
+    few-item case, several for the many-item case) still walk every key tile
+    of every segment, and the output equals the main kernel's bit for bit."""
+    lengths = [3000, 17, 512, 1300, 0, 129, 2049, 64] * repeats
+    wl = W.make_custom(lengths, H=8, D=128)
+    q, k, v = (t.cuda() for t in W.make_qkv(wl, seed=83))
+    cu, _ = oracle.pack(wl.seg, wl.n_seg)
+    dcu = torch.from_numpy(cu).cuda()
+    o_main = h3.varlen_attn_fwd(q, k, v, dcu, total_rows=wl.n, max_seqlen=0)
+    o_hint = h3.varlen_attn_fwd(q, k, v, dcu, total_rows=wl.n, max_seqlen=512)
+    torch.cuda.synchronize()
+    assert torch.equal(o_main[:wl.n], o_hint[:wl.n])
