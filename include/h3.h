@@ -282,19 +282,6 @@ h3_status h3_sigma_schedule(int32_t n_steps, double shift, double* out);
 h3_status h3_validate_seqlens(const int32_t* cu_seqlens, int32_t n_seg, int32_t capacity,
                               hipStream_t stream);
 
-/* ------------------------------------------------------------------------ */
-/* Diagnostic, not part of the path: sustained bf16 matrix-core throughput on
- * random operands (values uniform in [-0.5, 0.5), a different operand pair on
- * every v_mfma_f32_32x32x16_bf16).  Launches `workgroups` workgroups of 4
- * waves (two per CU put two waves on every SIMD, as the attention kernel
- * does); each wave issues iters * 8 MFMAs, so the call performs
- * workgroups * 4 * iters * 8 * 32768 FLOP.  `out` (device, caller-owned)
- * receives workgroups * 256 floats that only keep the work alive.  Time the
- * call with events on `stream`.  Errors: H3_ERR_NULL (out), H3_ERR_SHAPE
- * (workgroups or iters not in 1 .. 2^20, or workgroups * iters > 2^28, which
- * bounds a call to a fraction of a second). */
-h3_status h3_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, hipStream_t stream);
-
 const char* h3_status_string(h3_status s);
 const char* h3_version(void);
 

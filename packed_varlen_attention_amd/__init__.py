@@ -18,22 +18,18 @@ and VSA-style block-sparse attention over 64-row blocks:
   vsa_select(q, k, cu_seqlens, total_rows, topk, max_seqlen) -> top-k key blocks per query block
   vsa_attn_fwd(q, k, v, cu_seqlens, total_rows, sel, topk)    -> O over the kept blocks
 
-and one diagnostic, not on the path:
-
-  probe_mfma_bf16(workgroups, iters, out)            -> sustained bf16 MFMA work on random operands
-
 Build the library in-tree first: ``python -m packed_varlen_attention_amd.build``.
 """
 from ._lib import (H3Error, H3_BF16, H3_F32, TEXT, VIDEO, AUDIO, LIB_PATH, SIGNATURES, load,
                    status_string, version, pack_rope, varlen_attn_fwd, unpack_by_modality,
                    unpack_euler, sigma_schedule, vsa_blocks_bound, vsa_select, vsa_attn_fwd,
                    validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
-                   unpack_workspace_bytes, workspace, rope_cfg, probe_mfma_bf16, quantize_qk_fp8,
+                   unpack_workspace_bytes, workspace, rope_cfg, quantize_qk_fp8,
                    varlen_attn_fwd_fp8qk)
 
 __all__ = ["H3Error", "H3_BF16", "H3_F32", "TEXT", "VIDEO", "AUDIO", "LIB_PATH", "SIGNATURES",
            "load", "status_string", "version", "pack_rope", "varlen_attn_fwd",
            "unpack_by_modality", "unpack_euler", "sigma_schedule", "vsa_blocks_bound", "vsa_select",
            "vsa_attn_fwd", "validate_seqlens", "pack_workspace_bytes",
-           "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg", "probe_mfma_bf16",
+           "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg",
            "quantize_qk_fp8", "varlen_attn_fwd_fp8qk"]

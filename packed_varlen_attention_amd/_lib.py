@@ -57,7 +57,6 @@ SIGNATURES = {
     "h3_varlen_attn_fwd_fp8qk": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _c.c_int, _vp, _vp, _sz, _vp]),
     "h3_validate_seqlens": (_c.c_int, [_vp, _i32, _i32, _vp]),
-    "h3_probe_mfma_bf16": (_c.c_int, [_i32, _i32, _vp, _vp]),
     "h3_status_string": (_c.c_char_p, [_c.c_int]),
     "h3_version": (_c.c_char_p, []),
 }
@@ -415,16 +414,3 @@ def validate_seqlens(cu_seqlens, capacity: int, stream=None) -> int:
     lib = load()
     return int(lib.h3_validate_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, int(capacity),
                                        _stream(stream)))
-
-
-def probe_mfma_bf16(workgroups: int, iters: int, out, stream=None):
-    """h3_probe_mfma_bf16 (diagnostic): sustained bf16 MFMA work on random
-    operands; `out` is a float32 device tensor of workgroups * 256 elements.
-    Returns the FLOPs the call performs."""
-    torch = _torch()
-    lib = load()
-    if out.dtype != torch.float32 or out.numel() < workgroups * 256:
-        raise ValueError("out must be float32 with workgroups * 256 elements")
-    _check(lib.h3_probe_mfma_bf16(int(workgroups), int(iters), _ptr(out), _stream(stream)),
-           "h3_probe_mfma_bf16")
-    return float(workgroups) * 4 * iters * 8 * 32768.0

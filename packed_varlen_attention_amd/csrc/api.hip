@@ -46,15 +46,6 @@ const char* h3_status_string(h3_status s) {
   return "unknown status";
 }
 
-h3_status h3_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, hipStream_t stream) {
-  if (!out) return H3_ERR_NULL;
-  // at most 2^28 workgroup-iterations (~2.8e14 FLOP, a fraction of a second)
-  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20) ||
-      (int64_t)workgroups * iters > ((int64_t)1 << 28))
-    return H3_ERR_SHAPE;
-  return from_hip(h3::launch_mfma_probe(workgroups, iters, out, stream));
-}
-
 const char* h3_version(void) { return "h3 0.1.0 gfx950"; }
 
 size_t h3_pack_workspace_bytes(int32_t n, int32_t n_seg) {

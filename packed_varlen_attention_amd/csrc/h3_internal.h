@@ -84,9 +84,6 @@ hipError_t launch_unpack_euler(const void* o, const int32_t* perm, const uint8_t
                                const uint8_t* pinned, int n, int H, int D, bool bf16,
                                const EulerOut& eo, void* ws, hipStream_t stream);
 
-// ---- diagnostic (probe.hip) ------------------------------------------------
-hipError_t launch_mfma_probe(int workgroups, int iters, float* out, hipStream_t stream);
-
 // FP8 Q.K attention (attn_fp8.hip)
 hipError_t launch_quantize_qk_fp8(const void* q, const void* k, int rows, int H, float scale, uint8_t* q8,
                                   uint8_t* k8, uint8_t* qe, uint8_t* ke, hipStream_t stream);

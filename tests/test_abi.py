@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
@@ -203,15 +203,6 @@ def test_vsa_host_validation(lib):
     assert S(rows=0, q=None, k=None) == OK and A(n_seg=0, q=None, o=None) == OK
     assert lib.h3_vsa_blocks_bound(300, 2) == 5 + 2
     assert lib.h3_vsa_workspace_bytes(300, 2, 4) >= 2 * 7 * 4 * 128 * 4
-
-
-def test_probe_host_validation(lib):
-    # rejected before any launch: no device needed
-    assert lib.h3_probe_mfma_bf16(512, 10, None, None) == 1                 # H3_ERR_NULL
-    assert lib.h3_probe_mfma_bf16(0, 10, 0x1000, None) == 3                  # H3_ERR_SHAPE
-    assert lib.h3_probe_mfma_bf16(512, 0, 0x1000, None) == 3
-    assert lib.h3_probe_mfma_bf16((1 << 20) + 1, 10, 0x1000, None) == 3
-    assert lib.h3_probe_mfma_bf16(1 << 10, (1 << 18) + 1, 0x1000, None) == 3   # > 2^28 workgroup-iterations
 
 
 def test_fp8qk_host_validation(lib):

@@ -288,19 +288,6 @@ def test_empty_inputs_and_validation():
     assert h3.validate_seqlens(torch.tensor([1, 4], dtype=torch.int32, device=dev), 10) == 4
 
 
-def test_mfma_probe_runs_and_counts_flops():
-    # the diagnostic behind bench.py's sustained-MFMA figure: every workgroup
-    # writes its lanes, the values are finite and the FLOP count is as documented
-    wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
-    out = torch.full((wg * 256,), float("nan"), dtype=torch.float32, device="cuda")
-    fl = h3.probe_mfma_bf16(wg, 64, out)
-    torch.cuda.synchronize()
-    assert fl == wg * 4 * 64 * 8 * 32768.0
-    assert torch.isfinite(out).all()
-    with pytest.raises(h3.H3Error):
-        h3.probe_mfma_bf16(0, 64, out)
-
-
 def test_short_segment_kernel_matches_main_kernel_bit_for_bit():
     """Segments up to 512 rows with max_seqlen given, and few 128-row items
     (here 147 for 512 workgroup slots), go to the short-segment kernel
