@@ -16,7 +16,9 @@
  *     allocates, keeps no state between calls and is re-entrant.  Calls that
  *     need scratch memory take a caller workspace whose size the matching
  *     h3_*_workspace_bytes() function returns; its contents need not be
- *     initialised and are meaningless after the call.
+ *     initialised and are meaningless after the call.  The one exception is
+ *     h3_varlen_attn_fwd_noalloc, which uses a fixed library-held buffer per
+ *     GPU instead (see there).
  *   - Tensors are contiguous, token-major [rows][H][D], 16-byte aligned.
  *     Element type is given by h3_dtype (bf16 = IEEE bfloat16, f32 = float).
  *   - Work is enqueued on `stream` and the call returns without waiting,
@@ -50,7 +52,9 @@ typedef enum {
   H3_ERR_UNSUPPORTED = 6,  /* D not in {64, 128}, RoPE split invalid, bad scale */
   H3_ERR_HIP = 7,          /* a HIP launch or runtime call failed */
   H3_ERR_WORKSPACE = 8,    /* workspace NULL or smaller than required */
-  H3_ERR_ALIGN = 9         /* a tensor pointer is not 16-byte aligned */
+  H3_ERR_ALIGN = 9,        /* a tensor pointer is not 16-byte aligned */
+  H3_ERR_TOO_LARGE = 10    /* the problem exceeds the fixed scratch of a
+                              no-allocation entry point */
 } h3_status;
 
 /* Modality tags, one uint8 per token ([P1] section 三: discrete text / video /
@@ -135,6 +139,25 @@ h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
                              int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
                              float softmax_scale, void* o,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Attention without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as
+ * h3_varlen_attn_fwd (bit-identical output), but the attention's scratch (the
+ * per-segment tile list and its scan partials) lives in a buffer of
+ * H3_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the first call on that GPU until the process ends.  The call uses the
+ * copy of the current device (the stream must belong to it) and allocates
+ * nothing.  Returns H3_ERR_TOO_LARGE when h3_attn_workspace_bytes(total_rows,
+ * n_seg) exceeds H3_NOALLOC_SCRATCH_BYTES (more than 65,471 segments).
+ * Every call on one GPU shares that GPU's buffer: calls whose execution
+ * overlaps on one GPU (on two streams, or from two threads without ordering)
+ * race and give unspecified results; calls ordered on one stream are safe. */
+#define H3_NOALLOC_SCRATCH_BYTES 262144
+h3_status h3_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
+                                     int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                                     float softmax_scale, void* o, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Attention with FP8 Q and K.  [P1] section 五 keeps the DiT block being

@@ -5,6 +5,7 @@ The three calls of the path, each a thin wrapper over the C ABI of libh3.so
 
   pack_rope(q, k, v, tags, pos, seg, n_seg, rope, s)  -> packed Q', K', V, cu_seqlens, perm
   varlen_attn_fwd(q, k, v, cu_seqlens, total_rows)   -> O
+  varlen_attn_fwd_noalloc(...)                       -> the same O, library-held scratch, no allocation
   unpack_by_modality(o, perm, tags, n_per_mod)       -> per-modality outputs and row indices
 
 and the denoising-step epilogue that can take unpack's place:
@@ -21,14 +22,14 @@ and VSA-style block-sparse attention over 64-row blocks:
 Build the library in-tree first: ``python -m packed_varlen_attention_amd.build``.
 """
 from ._lib import (H3Error, H3_BF16, H3_F32, TEXT, VIDEO, AUDIO, LIB_PATH, SIGNATURES, load,
-                   status_string, version, pack_rope, varlen_attn_fwd, unpack_by_modality,
+                   status_string, version, pack_rope, varlen_attn_fwd, varlen_attn_fwd_noalloc, unpack_by_modality,
                    unpack_euler, sigma_schedule, vsa_blocks_bound, vsa_select, vsa_attn_fwd,
                    validate_seqlens, pack_workspace_bytes, attn_workspace_bytes,
                    unpack_workspace_bytes, workspace, rope_cfg, quantize_qk_fp8,
                    varlen_attn_fwd_fp8qk)
 
 __all__ = ["H3Error", "H3_BF16", "H3_F32", "TEXT", "VIDEO", "AUDIO", "LIB_PATH", "SIGNATURES",
-           "load", "status_string", "version", "pack_rope", "varlen_attn_fwd",
+           "load", "status_string", "version", "pack_rope", "varlen_attn_fwd", "varlen_attn_fwd_noalloc",
            "unpack_by_modality", "unpack_euler", "sigma_schedule", "vsa_blocks_bound", "vsa_select",
            "vsa_attn_fwd", "validate_seqlens", "pack_workspace_bytes",
            "attn_workspace_bytes", "unpack_workspace_bytes", "workspace", "rope_cfg",

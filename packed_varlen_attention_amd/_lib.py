@@ -39,6 +39,8 @@ SIGNATURES = {
     "h3_attn_workspace_bytes": (_sz, [_i32, _i32]),
     "h3_varlen_attn_fwd": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _c.c_int,
                                       _f32, _vp, _vp, _sz, _vp]),
+    "h3_varlen_attn_fwd_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _c.c_int,
+                                              _f32, _vp, _vp]),
     "h3_unpack_workspace_bytes": (_sz, [_i32]),
     "h3_unpack_by_modality": (_c.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _c.c_int,
                                          _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_i32),
@@ -223,6 +225,30 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, total_rows: int, max_seqlen: int = 0,
                                 int(total_rows), H, D, _dt(q), float(softmax_scale), _ptr(o),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "h3_varlen_attn_fwd")
+    return o
+
+
+def varlen_attn_fwd_noalloc(q, k, v, cu_seqlens, total_rows: int, max_seqlen: int = 0,
+                            softmax_scale: float = 0.0, *, o=None, stream=None):
+    """h3_varlen_attn_fwd_noalloc: the same attention with the library's fixed
+    per-GPU scratch instead of a workspace (the library allocates nothing;
+    calls that overlap on one GPU race).  Returns o."""
+    torch = _torch()
+    lib = load()
+    rows, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if total_rows > rows:
+        raise ValueError("total_rows exceeds the tensors' rows")
+    n_seg = cu_seqlens.shape[0] - 1
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib.h3_varlen_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), n_seg, int(max_seqlen),
+                                        int(total_rows), H, D, _dt(q), float(softmax_scale), _ptr(o),
+                                        _stream(stream))
+    _check(st, "h3_varlen_attn_fwd_noalloc")
     return o
 
 

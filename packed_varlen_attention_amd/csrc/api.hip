@@ -4,9 +4,16 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <vector>
 
 #include "h3_internal.h"
+
+// Scratch of h3_varlen_attn_fwd_noalloc: one copy per GPU, resident until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: host code only ever uses the address hipGetSymbolAddress returns
+// for the current device (noalloc_scratch below).
+static __device__ __align__(256) char scratch[H3_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -26,6 +33,57 @@ h3_status check_dims(int32_t H, int32_t D, h3_dtype dt) {
 
 h3_status from_hip(hipError_t e) { return e == hipSuccess ? H3_OK : H3_ERR_HIP; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+h3_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return H3_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return H3_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return H3_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return H3_OK;
+}
+
+// Host checks of the attention call that do not involve the workspace.
+// Returns H3_OK with *nothing = true for an empty problem.
+h3_status attn_checks(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_seg,
+                      int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                      float softmax_scale, const void* o, bool* nothing) {
+  *nothing = false;
+  h3_status st = check_dims(H, D, dt);
+  if (st != H3_OK) return st;
+  if (n_seg < 0 || total_rows < 0 || max_seqlen < 0 || total_rows > kMaxRows) return H3_ERR_SHAPE;
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale)) return H3_ERR_UNSUPPORTED;
+  if (total_rows == 0 || n_seg == 0) {
+    *nothing = true;
+    return H3_OK;
+  }
+  if (!q || !k || !v || !o || !cu_seqlens) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3_ERR_ALIGN;
+  return H3_OK;
+}
+
+h3_status attn_dispatch(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_seg,
+                        int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                        float softmax_scale, void* o, void* workspace, hipStream_t stream) {
+  const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)D));
+  if (dt == H3_BF16)
+    return from_hip(h3::launch_attn_bf16(q, k, v, o, cu_seqlens, n_seg, max_seqlen, total_rows, H, D,
+                                         scale, workspace, stream));
+  return from_hip(h3::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), static_cast<float*>(o), cu_seqlens,
+                                      n_seg, total_rows, H, D, scale, workspace, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -42,6 +100,7 @@ const char* h3_status_string(h3_status s) {
     case H3_ERR_HIP: return "HIP launch or runtime error";
     case H3_ERR_WORKSPACE: return "workspace missing or too small";
     case H3_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case H3_ERR_TOO_LARGE: return "problem exceeds the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -102,22 +161,32 @@ h3_status h3_varlen_attn_fwd(const void* q, const void* k, const void* v,
                              int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
                              float softmax_scale, void* o,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  h3_status st = check_dims(H, D, dt);
-  if (st != H3_OK) return st;
-  if (n_seg < 0 || total_rows < 0 || max_seqlen < 0 || total_rows > kMaxRows) return H3_ERR_SHAPE;
-  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale)) return H3_ERR_UNSUPPORTED;
-  if (total_rows == 0 || n_seg == 0) return H3_OK;
-  if (!q || !k || !v || !o || !cu_seqlens) return H3_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3_ERR_ALIGN;
+  bool nothing = false;
+  h3_status st = attn_checks(q, k, v, cu_seqlens, n_seg, max_seqlen, total_rows, H, D, dt, softmax_scale, o,
+                             &nothing);
+  if (st != H3_OK || nothing) return st;
   if (!workspace || workspace_bytes < h3::attn_workspace_bytes(total_rows, n_seg))
     return H3_ERR_WORKSPACE;
-  const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)D));
-  if (dt == H3_BF16)
-    return from_hip(h3::launch_attn_bf16(q, k, v, o, cu_seqlens, n_seg, max_seqlen, total_rows, H, D,
-                                         scale, workspace, stream));
-  return from_hip(h3::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                      static_cast<const float*>(v), static_cast<float*>(o), cu_seqlens,
-                                      n_seg, total_rows, H, D, scale, workspace, stream));
+  return attn_dispatch(q, k, v, cu_seqlens, n_seg, max_seqlen, total_rows, H, D, dt, softmax_scale, o, workspace,
+                       stream);
+}
+
+h3_status h3_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
+                                     int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                                     float softmax_scale, void* o, hipStream_t stream) {
+  bool nothing = false;
+  h3_status st = attn_checks(q, k, v, cu_seqlens, n_seg, max_seqlen, total_rows, H, D, dt, softmax_scale, o,
+                             &nothing);
+  if (st != H3_OK || nothing) return st;
+  if (h3::attn_workspace_bytes(total_rows, n_seg) > (size_t)H3_NOALLOC_SCRATCH_BYTES) return H3_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != H3_OK) return st;
+  // The tile list and the scan partials in the scratch are fully rewritten
+  // by every call before they are read: nothing needs clearing.
+  return attn_dispatch(q, k, v, cu_seqlens, n_seg, max_seqlen, total_rows, H, D, dt, softmax_scale, o, ws,
+                       stream);
 }
 
 h3_status h3_quantize_qk_fp8(const void* q, const void* k, int32_t rows, int32_t H, int32_t D, h3_dtype dt,

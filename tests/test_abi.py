@@ -15,7 +15,7 @@ from packed_varlen_attention_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "h3.h")
 
-OK, NULL, DTYPE, SHAPE, SEQLENS, CAPACITY, UNSUPPORTED, HIP, WORKSPACE, ALIGN = range(10)
+OK, NULL, DTYPE, SHAPE, SEQLENS, CAPACITY, UNSUPPORTED, HIP, WORKSPACE, ALIGN, TOO_LARGE = range(11)
 
 
 def header_functions():
@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.SIGNATURES) == names      # the binding declares the same set
@@ -42,11 +42,11 @@ def test_exports_every_declared_function(lib):
 def test_version_and_status_strings(lib):
     assert "gfx950" in h3.version()
     seen = set()
-    for s in range(10):
+    for s in range(11):
         msg = h3.status_string(s)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert h3.status_string(99) == "unknown status"
 
 
@@ -88,6 +88,29 @@ def test_attn_host_validation(lib):
     # empty problems are a no-op success, nothing launched
     assert _attn(lib, rows=0, q=None, k=None, v=None, o=None) == OK
     assert _attn(lib, n_seg=0, q=None, k=None, v=None, o=None) == OK
+
+
+def _attn_na(lib, q=P, k=P, v=P, cu=P, n_seg=2, max_seqlen=64, rows=100, H=4, D=128, dt=0, scale=0.0, o=P):
+    return lib.h3_varlen_attn_fwd_noalloc(q, k, v, cu, n_seg, max_seqlen, rows, H, D, dt, scale, o, None)
+
+
+def test_attn_noalloc_host_validation(lib):
+    """The no-allocation entry point makes the same host checks, and rejects a
+    segment count whose tile list does not fit its fixed scratch, before it
+    touches any device (these calls run without a GPU)."""
+    assert _attn_na(lib, D=96) == UNSUPPORTED
+    assert _attn_na(lib, dt=7) == DTYPE
+    assert _attn_na(lib, H=0) == SHAPE
+    assert _attn_na(lib, rows=-1) == SHAPE
+    assert _attn_na(lib, scale=float("nan")) == UNSUPPORTED
+    assert _attn_na(lib, v=None) == NULL
+    assert _attn_na(lib, q=MIS) == ALIGN
+    assert _attn_na(lib, rows=0, q=None, k=None, v=None, o=None) == OK
+    limit = 262144
+    assert lib.h3_attn_workspace_bytes(1 << 20, 65471) <= limit < lib.h3_attn_workspace_bytes(1 << 20, 65472)
+    assert _attn_na(lib, n_seg=65472, rows=1 << 20) == TOO_LARGE
+    assert _attn_na(lib, n_seg=1 << 20, rows=1 << 20) == TOO_LARGE
+    assert "no-allocation" in h3.status_string(TOO_LARGE)
 
 
 def _pack(lib, n=10, n_seg=2, H=2, D=128, dt=0, cap=16, rope="default", s=0.0, qs=P, qo=P, vo=P,
