@@ -30,9 +30,10 @@ COMMON_FLAGS = [
     # this, one-wave-per-SIMD kernels put every accumulator in AGPRs and copy
     # the softmax inputs back out on every tile.
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-    # Nothing on this path propagates NaN through min/max (pad rows are never
-    # read; masked keys are -inf), so max needs no quieting instructions.
-    "-fno-honor-nans",
+    # Nothing on the kernels' path propagates NaN through min/max (pad rows are
+    # never read; masked keys are -inf), so max needs no quieting instructions.
+    # Device code only: the host pass keeps its NaN checks of the arguments.
+    "-Xarch_device", "-fno-honor-nans",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

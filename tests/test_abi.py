@@ -142,6 +142,40 @@ def test_pack_host_validation(lib):
     assert _pack(lib, rope=bad) == UNSUPPORTED
 
 
+def test_host_checks_reject_nan_arguments(lib):
+    """Every floating-point argument the host validates rejects NaN (the
+    device-only -fno-honor-nans must not reach these host checks)."""
+    nan = float("nan")
+    assert _pack(lib, s=nan) == UNSUPPORTED                       # time offset s
+    assert _pack(lib, s=float("-inf")) == UNSUPPORTED
+    for m in range(3):
+        bad = _rope(128)
+        bad.m[m].base = nan
+        assert _pack(lib, rope=bad) == UNSUPPORTED
+        bad = _rope(128)
+        bad.m[m].time_scale = nan
+        assert _pack(lib, rope=bad) == UNSUPPORTED
+        bad = _rope(128)
+        bad.m[m].base = float("inf")
+        assert _pack(lib, rope=bad) == UNSUPPORTED
+    assert _attn(lib, scale=nan) == UNSUPPORTED
+    assert _attn(lib, scale=float("inf")) == UNSUPPORTED
+    assert _attn_na(lib, scale=nan) == UNSUPPORTED
+    for i in range(3):
+        sig = [0.9, 0.9, 0.9]
+        sig[i] = nan
+        assert _euler(lib, sig=tuple(sig)) == UNSUPPORTED
+        nxt = [0.8, 0.8, 0.8]
+        nxt[i] = nan
+        assert _euler(lib, nxt=tuple(nxt)) == UNSUPPORTED
+    out = (ctypes.c_double * 2)()
+    assert lib.h3_sigma_schedule(1, nan, out) == UNSUPPORTED
+    assert lib.h3_quantize_qk_fp8(P, P, 300, 4, 128, 0, nan, P, P, P, P, None) == UNSUPPORTED
+    assert lib.h3_vsa_select(P, P, P, 2, 256, 300, 4, 128, 0, nan, 4, P, None, None, P, 1 << 30, None) \
+        == UNSUPPORTED
+    assert lib.h3_vsa_attn_fwd(P, P, P, P, 2, 300, 4, 128, 0, nan, P, 4, P, P, 1 << 30, None) == UNSUPPORTED
+
+
 def test_unpack_host_validation(lib):
     out = (ctypes.c_void_p * 3)(P, P, P)
     idx = (ctypes.c_void_p * 3)(P, P, P)
