@@ -89,14 +89,16 @@ typedef struct { h3_rope_modality m[3]; } h3_rope_cfg;   /* indexed by h3_modali
  *                         outside 0..2 leaves that row unrotated.
  *   pos_thw             : int32 [n][3], (t, h, w) per token (device)
  *   seg_id              : int32 [n], sub-sequence of each token, 0..n_seg-1
- *                         (device).  A token with an id outside that range is
- *                         dropped (then cu_seqlens[n_seg] < n).
+ *                         (device).  A token with an id outside that range
+ *                         belongs to no sub-sequence and gets no packed row
+ *                         (then cu_seqlens[n_seg] < n).
  *   rope                : host struct; time_offset_frames = s of the shift.
  *   q_out, k_out        : [capacity][H][D] packed, Q and K rotated (device)
  *   v_out               : [capacity][H][D] packed V, or NULL to skip V
  *   cu_seqlens          : int32 [n_seg+1] out: cu[0] = 0, segment k occupies
  *                         packed rows [cu[k], cu[k+1])
  *   perm                : int32 [n] out: perm[p] = source row at packed row p
+ *                         for p < cu_seqlens[n_seg], -1 from there to n
  * Packed order is the stable order by segment id: rows of one segment keep
  * their source order.  Rows [cu[n_seg], capacity) are not written.
  * Requires n <= capacity; n = 0 is a no-op apart from cu_seqlens = 0.
@@ -210,6 +212,8 @@ h3_status h3_varlen_attn_fwd_fp8qk(const uint8_t* q8, const uint8_t* qe, const u
  *   n_per_mod  : host int32[3], number of tokens with tag m
  * For modality m, token k (k-th token of tag m in source order) gets
  * idx[m][k] = packed row p with perm[p] = its source row, and out[m][k] = o[p].
+ * A token that no perm entry names (the pack gave it no packed row; entries
+ * < 0 name no token) keeps its slot: idx[m][k] = -1, out[m][k] not written.
  * Exact copy: no arithmetic on values. */
 size_t h3_unpack_workspace_bytes(int32_t n);
 h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_t* tags_src,
@@ -237,9 +241,10 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
  * blocks of b's segment (equal scores: lower block first), in increasing block
  * order, -1 where the segment has fewer blocks.  Rows of sel past the real
  * block count are not written.  qmean, kmean (optional, fp32
- * [nb_cap][H][D]) receive the block means.  max_seqlen (host) must be >=
- * every segment length: a segment with more than ceil(max_seqlen / 64)
- * blocks is scored on its first ones only; max_seqlen <= 1,048,576.
+ * [nb_cap][H][D]) receive the block means.  max_seqlen (host) is a hint of
+ * the longest segment (0 = unknown) that sizes the scores' on-chip buffer;
+ * results do not depend on it (a longer segment is scored by a slower path
+ * that gives the same selection).
  *
  * h3_vsa_attn_fwd: every row of query block b, head h, attends to the keys of
  * the blocks listed in sel[h][b] (entries < 0 end the list; blocks outside
@@ -282,7 +287,9 @@ h3_status h3_vsa_attn_fwd(const void* q, const void* k, const void* v, const int
  *                modality m are set to them (NULL: pinned rows keep z)
  *   sigma[m], sigma_next[m] : host, this step's noise levels of modality m
  * Non-pinned rows: z += (float)(sigma_next - sigma) * v, one fp32 fma per
- * element.  Workspace: h3_unpack_workspace_bytes(n). */
+ * element.  A token without a packed row (see h3_unpack_by_modality) has no
+ * velocity: its state row is left as it is and its idx is -1.
+ * Workspace: h3_unpack_workspace_bytes(n). */
 h3_status h3_unpack_euler(const void* o, const int32_t* perm, const uint8_t* tags_src,
                           const uint8_t* pinned_src, int32_t n, int32_t H, int32_t D, h3_dtype dt,
                           float* const z[3], const float* const anchor[3],

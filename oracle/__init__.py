@@ -24,7 +24,9 @@ Steps and the passages they follow:
   block_means,
   vsa_scores,
   vsa_select,
-  vsa_attention   [P3] sparse-attention section, VSA (64-token blocks, block
+  vsa_attention,
+  vsa_attention_blocks
+                  [P3] sparse-attention section, VSA (64-token blocks, block
                   relevance score, top-k blocks kept, attention among the kept
                   blocks); the gate is a stand-in (block-mean dot product)
   sigma_schedule,
@@ -64,7 +66,7 @@ permuting keys inside a kept block.  No function here is "parity unpinned".
 from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
                         attention, attention_rows, attention_weights, unpack, run,
                         rope_qk, sigma_schedule, x0_from_velocity, euler_step, unpack_euler,
-                        block_layout, block_means, vsa_scores, vsa_select, vsa_attention,
+                        block_layout, block_means, vsa_scores, vsa_select, vsa_attention, vsa_attention_blocks,
                         E4M3_MAX, e4m3_value, e4m3_round, mx_exponent, quantize_mx_e4m3,
                         dequantize_mx_e4m3, fp8qk_inputs, attention_base2, attention_base2_rows,
                         attention_fp8qk)
@@ -72,7 +74,7 @@ from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply
 __all__ = ["TEXT", "VIDEO", "AUDIO", "pack", "time_shift", "rope_angles", "apply_rope",
            "attention", "attention_rows", "attention_weights", "unpack", "run", "rope_qk",
            "sigma_schedule", "x0_from_velocity", "euler_step", "unpack_euler",
-           "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention",
+           "block_layout", "block_means", "vsa_scores", "vsa_select", "vsa_attention", "vsa_attention_blocks",
            "E4M3_MAX", "e4m3_value", "e4m3_round", "mx_exponent", "quantize_mx_e4m3",
            "dequantize_mx_e4m3", "fp8qk_inputs", "attention_base2", "attention_base2_rows",
            "attention_fp8qk"]

@@ -22,11 +22,15 @@ def pack(seg: np.ndarray, n_seg: int):
 
     Returns (cu_seqlens int32 [n_seg+1], perm int32 [n]) where perm[p] is the
     source row placed at packed row p and segment k occupies packed rows
-    [cu[k], cu[k+1]).  Tokens of one segment keep their source order.
+    [cu[k], cu[k+1]).  Tokens of one segment keep their source order.  A
+    token whose segment id is outside 0..n_seg-1 belongs to no sub-sequence:
+    it gets no packed row, and perm is -1 from cu[n_seg] on.
     """
     seg = np.asarray(seg, np.int64)
-    perm = np.argsort(seg, kind="stable").astype(np.int32)
-    counts = np.bincount(seg, minlength=n_seg)[:n_seg]
+    kept = np.nonzero((seg >= 0) & (seg < n_seg))[0]
+    perm = np.full(seg.shape[0], -1, np.int32)
+    perm[:kept.shape[0]] = kept[np.argsort(seg[kept], kind="stable")]
+    counts = np.bincount(seg[kept], minlength=n_seg)[:n_seg]
     cu = np.zeros(n_seg + 1, np.int64)
     cu[1:] = np.cumsum(counts)
     return cu.astype(np.int32), perm
@@ -175,17 +179,25 @@ def attention_weights(q, k, cu, softmax_scale: Optional[float] = None):
 # ---------------------------------------------------------------------------
 def unpack(o, perm, tags):
     """For each modality m (text, video, audio): idx_m lists the packed row of
-    every source token with tag m, in source order, and out_m = o[idx_m]."""
+    every source token with tag m, in source order, and out_m = o[idx_m].  A
+    token with no packed row (perm entries < 0 mark packed rows that hold no
+    token) keeps its place in its modality's slice, with index -1 and a NaN
+    row (no value)."""
     perm = np.asarray(perm, np.int64)
-    inv = np.empty_like(perm)
-    inv[perm] = np.arange(perm.shape[0])
+    n = perm.shape[0]
+    inv = np.full(n, -1, np.int64)
+    placed = np.nonzero(perm >= 0)[0]
+    inv[perm[placed]] = placed
     tags = np.asarray(tags)
     outs, idxs = [], []
     for m in (TEXT, VIDEO, AUDIO):
         src = np.nonzero(tags == m)[0]
         idx = inv[src]
+        out = np.full((src.shape[0],) + tuple(o.shape[1:]), np.nan)
+        have = idx >= 0
+        out[have] = o[idx[have]]
         idxs.append(idx.astype(np.int32))
-        outs.append(o[idx])
+        outs.append(out)
     return outs, idxs
 
 
@@ -279,6 +291,31 @@ def vsa_attention(q, k, v, cu, sel, block: int = 64, softmax_scale: Optional[flo
             P = P / P.sum(axis=1, keepdims=True)
             o[r0:r1, h, :] = P @ v[keys, h, :]
     return o
+
+
+def vsa_attention_blocks(q, k, v, cu, sel, blocks: Sequence[int], heads: Optional[Sequence[int]] = None,
+                         block: int = 64, softmax_scale: Optional[float] = None):
+    """vsa_attention evaluated only for the query blocks `blocks` and heads
+    `heads` (indices into q's head axis; sel is indexed by position in
+    `heads`): a list over `blocks` of float64 [rows of the block,
+    len(heads), D]."""
+    rows, H, D = q.shape
+    sc = _scale(D, softmax_scale)
+    heads = np.arange(H) if heads is None else np.asarray(heads, np.int64)
+    bstart, _, _ = block_layout(cu, block)
+    out = []
+    for b in blocks:
+        r0, r1 = int(bstart[b]), int(bstart[b + 1])
+        ob = np.zeros((r1 - r0, heads.shape[0], D), np.float64)
+        for hi, h in enumerate(heads):
+            keys = np.concatenate([np.arange(bstart[c], bstart[c + 1]) for c in sel[hi, b] if c >= 0])
+            S = (q[r0:r1, h, :] @ k[keys, h, :].T) * sc
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P = P / P.sum(axis=1, keepdims=True)
+            ob[:, hi, :] = P @ v[keys, h, :]
+        out.append(ob)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -476,7 +513,8 @@ def unpack_euler(o, perm, tags, z, sigma, sigma_next, pinned_src=None, anchor=No
     """Stage 4 slicing followed by stages 5-7 per modality: for modality m with
     a state z[m] ([n_m, ...], tokens of tag m in source order), the velocity
     rows are o[idx_m] (unpack) and the state steps with (sigma[m],
-    sigma_next[m]).  pinned_src: bool [n] in source order.  Returns the new
+    sigma_next[m]).  pinned_src: bool [n] in source order.  A token with no
+    packed row has no velocity: its state is left as it is.  Returns the new
     states (None where z[m] is None) and idx."""
     outs, idxs = unpack(o, perm, tags)
     tags = np.asarray(tags)
@@ -488,8 +526,11 @@ def unpack_euler(o, perm, tags, z, sigma, sigma_next, pinned_src=None, anchor=No
         pin = None
         if pinned_src is not None:
             pin = np.asarray(pinned_src, bool)[np.nonzero(tags == m)[0]]
-        new.append(euler_step(z[m], outs[m], sigma[m], sigma_next[m], pin,
-                              None if anchor is None else anchor[m]))
+        vel = outs[m].copy()
+        vel[idxs[m] < 0] = 0.0                      # no packed row: placeholder, overwritten below
+        step = euler_step(z[m], vel, sigma[m], sigma_next[m], pin, None if anchor is None else anchor[m])
+        step[idxs[m] < 0] = np.asarray(z[m], np.float64)[idxs[m] < 0]
+        new.append(step)
     return new, idxs
 
 
@@ -504,7 +545,8 @@ def run(q_src, k_src, v_src, tags, pos, seg, n_seg, rope, time_offset,
     outs (per modality) and idxs (per modality)."""
     cu, perm = pack(seg, n_seg)
     qr, kr = rope_qk(q_src, k_src, tags, pos, rope, time_offset)
-    qp, kp, vp = qr[perm], kr[perm], v_src[perm]
+    placed = perm[:cu[-1]]                          # tokens with a packed row
+    qp, kp, vp = qr[placed], kr[placed], v_src[placed]
     o = attention(qp, kp, vp, cu, softmax_scale)
     outs, idxs = unpack(o, perm, tags)
     return dict(cu=cu, perm=perm, q=qp, k=kp, v=vp, o=o, outs=outs, idxs=idxs)

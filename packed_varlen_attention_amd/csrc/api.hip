@@ -311,9 +311,6 @@ size_t h3_vsa_workspace_bytes(int32_t total_rows, int32_t n_seg, int32_t H) {
 }
 
 namespace {
-// Key blocks of one segment that the selection keeps in LDS (64 KB of scores).
-constexpr int32_t kVsaMaxSegmentBlocks = 16384;
-
 h3_status vsa_common_checks(int32_t n_seg, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, float scale,
                             int32_t topk) {
   h3_status st = check_dims(H, D, dt);
@@ -332,7 +329,6 @@ h3_status h3_vsa_select(const void* q, const void* k, const int32_t* cu_seqlens,
   h3_status st = vsa_common_checks(n_seg, total_rows, H, D, dt, softmax_scale, topk);
   if (st != H3_OK) return st;
   if (max_seqlen < 0) return H3_ERR_SHAPE;
-  if ((max_seqlen + 63) / 64 > kVsaMaxSegmentBlocks) return H3_ERR_UNSUPPORTED;
   if (total_rows == 0 || n_seg == 0) return H3_OK;
   if (!q || !k || !cu_seqlens || !sel) return H3_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || (qmean && !aligned16(qmean)) || (kmean && !aligned16(kmean)))

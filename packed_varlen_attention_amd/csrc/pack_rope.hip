@@ -14,7 +14,8 @@
 //      every pair, the packed row of its first token; row 0 of each segment
 //      is cu_seqlens[segment];
 //   3. move pass: one workgroup per source token computes its packed row,
-//      records perm, computes the token's D/2 rotation angles once (fp64
+//      records perm (tokens whose segment id is out of range are dropped; perm
+//      is -1 on the packed rows past the last segment), computes the token's D/2 rotation angles once (fp64
 //      angle and cos/sin) and streams Q, K, V of all heads with 16-byte
 //      coalesced loads and stores, rotating Q and K in fp32 and rounding once.
 #include "h3_internal.h"
@@ -80,10 +81,15 @@ __global__ __launch_bounds__(kRankBlock) void pack_rank_kernel(const int32_t* __
   if (before == total - 1) table[(int64_t)my * nblk + blockIdx.x] = total;
 }
 
+// cu_seqlens from the scanned table.  Packed rows from cu[n_seg] to n hold no
+// token (their tokens' segment ids were out of range): perm = -1 there.
 __global__ void write_cu_kernel(const int32_t* __restrict__ table, int n_seg, int nblk,
-                                const int32_t* __restrict__ total, int32_t* __restrict__ cu) {
-  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s <= n_seg; s += gridDim.x * blockDim.x)
-    cu[s] = (s == n_seg) ? *total : table[(int64_t)s * nblk];
+                                const int32_t* __restrict__ total, int32_t* __restrict__ cu,
+                                int32_t* __restrict__ perm, int n) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+  const int packed = min(max(*total, 0), n);
+  for (int s = tid; s <= n_seg; s += stride) cu[s] = (s == n_seg) ? packed : table[(int64_t)s * nblk];
+  for (int p = packed + tid; p < n; p += stride) perm[p] = -1;
 }
 
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
@@ -243,7 +249,7 @@ hipError_t launch_pack_rope(const void* q_src, const void* k_src, const void* v_
   hipError_t e = exclusive_scan_i32(table, table_n, total, scan_ws, stream);
   if (e != hipSuccess) return e;
   const unsigned cu_blocks = (unsigned)std::min<int64_t>(1024, ceil_div((int64_t)n_seg + 1, 256));
-  write_cu_kernel<<<cu_blocks, 256, 0, stream>>>(table, n_seg, nblk, total, cu);
+  write_cu_kernel<<<cu_blocks, 256, 0, stream>>>(table, n_seg, nblk, total, cu, perm, n);
   if (bf16)
     pack_move_kernel<true><<<n, kMoveThreads, 0, stream>>>(q_src, k_src, v_src, tags, pos, seg, n_seg,
                                                           nblk, H, D, rope, table, local_rank,

@@ -13,7 +13,9 @@
 //      start turns it into per-modality offsets;
 //   3. move pass: one workgroup per packed row p: source row i = perm[p],
 //      modality m = tags[i], rank k -> idx[m][k] = p, out[m][k] = o[p]
-//      (16-byte coalesced row copy, no arithmetic on values).
+//      (16-byte coalesced row copy, no arithmetic on values).  Rows with
+//      perm[p] < 0 hold no token; a token without a packed row keeps its slot
+//      with idx -1 (written by pass 1) and an unwritten out row.
 //
 // The Euler epilogue ([P1] section 四, runtime loop stages 5-7: the
 // rectified-flow velocity gives x0 = z - sigma v, the eta = 0 Euler step
@@ -30,13 +32,28 @@ namespace {
 
 constexpr int kMoveThreads = 128;
 
+// Index outputs, pre-filled with -1 by the rank pass: a token with no packed
+// row (dropped by the pack) keeps -1, every other slot is overwritten by the
+// move pass that runs after it.
+struct IdxFill {
+  int32_t* idx[3];
+  int32_t n[3];
+};
+
 __global__ __launch_bounds__(kRankBlock) void unpack_rank_kernel(const uint8_t* __restrict__ tags, int n,
                                                                  int nblk, int32_t* __restrict__ table,
-                                                                 int32_t* __restrict__ local_rank) {
+                                                                 int32_t* __restrict__ local_rank,
+                                                                 IdxFill fill) {
   constexpr int kWaves = kRankBlock / 64;
   __shared__ int32_t wave_cnt[kWaves][3];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = blockIdx.x * kRankBlock + threadIdx.x;
+  {
+    // slot i of the three index arrays laid end to end (their total is <= n)
+    int j = i, mm = 0;
+    while (mm < 3 && j >= fill.n[mm]) j -= fill.n[mm++];
+    if (mm < 3 && fill.idx[mm]) fill.idx[mm][j] = -1;
+  }
   const int m = (i < n) ? (int)tags[i] : 3;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int rank = 0;
@@ -158,7 +175,9 @@ hipError_t launch_unpack(const void* o, const int32_t* perm, const uint8_t* tags
   w += align_up((size_t)(3 * nblk) * 4, 256);
   int32_t* local_rank = reinterpret_cast<int32_t*>(w);
   w += align_up((size_t)n * 4, 256);
-  unpack_rank_kernel<<<nblk, kRankBlock, 0, stream>>>(tags, n, nblk, table, local_rank);
+  const IdxFill fill{{outs.idx[0], outs.idx[1], outs.idx[2]},
+                     {outs.n_per_mod[0], outs.n_per_mod[1], outs.n_per_mod[2]}};
+  unpack_rank_kernel<<<nblk, kRankBlock, 0, stream>>>(tags, n, nblk, table, local_rank, fill);
   hipError_t e = exclusive_scan_i32(table, 3 * (int64_t)nblk, nullptr, w, stream);
   if (e != hipSuccess) return e;
   const int64_t row_bytes = (int64_t)H * D * elem_bytes;
@@ -177,7 +196,8 @@ hipError_t launch_unpack_euler(const void* o, const int32_t* perm, const uint8_t
   w += align_up((size_t)(3 * nblk) * 4, 256);
   int32_t* local_rank = reinterpret_cast<int32_t*>(w);
   w += align_up((size_t)n * 4, 256);
-  unpack_rank_kernel<<<nblk, kRankBlock, 0, stream>>>(tags, n, nblk, table, local_rank);
+  const IdxFill fill{{eo.idx[0], eo.idx[1], eo.idx[2]}, {eo.n_per_mod[0], eo.n_per_mod[1], eo.n_per_mod[2]}};
+  unpack_rank_kernel<<<nblk, kRankBlock, 0, stream>>>(tags, n, nblk, table, local_rank, fill);
   hipError_t e = exclusive_scan_i32(table, 3 * (int64_t)nblk, nullptr, w, stream);
   if (e != hipSuccess) return e;
   const int64_t row_elems = (int64_t)H * D;

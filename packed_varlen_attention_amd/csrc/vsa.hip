@@ -127,12 +127,13 @@ __device__ int block_excl_scan(int x, int* buf, int* total) {
 }
 
 // Top-k of one query block's keys (order_key of its scores, one per key
-// block of its segment, in LDS): writes the kept global block numbers cb0 + c
-// in increasing order to out[0 .. min(topk, n_kb)) and -1 to the rest.  Keys
-// larger than the k-th largest are all kept; among keys equal to it, the
-// lowest block indices.  Called by all kSelThreads threads; ends with the
-// writes (callers that reuse the LDS afterwards put a barrier first).
-__device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int topk, int cb0, int32_t* out,
+// block of its segment; key_at(c) returns key c): writes the kept global block
+// numbers cb0 + c in increasing order to out[0 .. min(topk, n_kb)) and -1 to
+// the rest.  Keys larger than the k-th largest are all kept; among keys equal
+// to it, the lowest block indices.  Called by all kSelThreads threads; ends
+// with the writes (callers that reuse the LDS afterwards put a barrier first).
+template <class KeyAt>
+__device__ __forceinline__ void select_topk(const KeyAt& key_at, int n_kb, int topk, int cb0, int32_t* out,
                                             int* s_hist, int* s_scan, uint32_t& s_prefix, int& s_need) {
   const int tid = threadIdx.x;
   if (tid == 0) { s_prefix = 0u; s_need = min(topk, n_kb); }
@@ -150,7 +151,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int 
       __syncthreads();
       const uint32_t pre = s_prefix;
       for (int c = tid; c < n_kb; c += kSelThreads) {
-        const uint32_t key = keys[c];
+        const uint32_t key = key_at(c);
         if ((key & hi_mask) == pre) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
@@ -196,7 +197,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int 
   const int c_lo = min(tid * chunk, n_kb), c_hi = min(c_lo + chunk, n_kb);
   int n_eq = 0;
   if (n_kb > topk)
-    for (int c = c_lo; c < c_hi; ++c) n_eq += keys[c] == thresh;
+    for (int c = c_lo; c < c_hi; ++c) n_eq += key_at(c) == thresh;
   int tot;
   const int eq_before = block_excl_scan(n_eq, s_scan, &tot);
   // count kept per thread (equal keys: by their rank among equal keys)
@@ -204,7 +205,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int 
   {
     int eq_rank = eq_before;
     for (int c = c_lo; c < c_hi; ++c) {
-      const uint32_t key = keys[c];
+      const uint32_t key = key_at(c);
       bool keep;
       if (n_kb <= topk) keep = true;
       else if (key > thresh) keep = true;
@@ -217,7 +218,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int 
   {
     int eq_rank = eq_before, pos = keep_before;
     for (int c = c_lo; c < c_hi; ++c) {
-      const uint32_t key = keys[c];
+      const uint32_t key = key_at(c);
       bool keep;
       if (n_kb <= topk) keep = true;
       else if (key > thresh) keep = true;
@@ -228,6 +229,37 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n_kb, int 
   }
   for (int i = need_total + tid; i < topk; i += kSelThreads) out[i] = -1;
 }
+
+// Keys already scored into LDS.
+struct LdsKeys {
+  const uint32_t* keys;
+  __device__ uint32_t operator()(int c) const { return keys[c]; }
+};
+
+// Keys scored on demand, for a segment whose key blocks do not fit the LDS
+// the launch sized from the max_seqlen hint: key c is the score of key block
+// cb0 + c against the scaled query mean sq (in LDS), with the fmaf order of
+// the LDS path, so both give identical keys (the radix select reads every key
+// five times, each time recomputed).
+struct ScoredKeys {
+  const float* kmean;
+  int64_t cb0;
+  int H, h;
+  const float* sq;
+  __device__ uint32_t operator()(int c) const {
+    const float4* km = reinterpret_cast<const float4*>(kmean + ((cb0 + c) * H + h) * 128);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d4 = 0; d4 < 32; ++d4) {
+      const float4 x = km[d4];
+      acc = fmaf(x.x, sq[4 * d4], acc);
+      acc = fmaf(x.y, sq[4 * d4 + 1], acc);
+      acc = fmaf(x.z, sq[4 * d4 + 2], acc);
+      acc = fmaf(x.w, sq[4 * d4 + 3], acc);
+    }
+    return order_key(acc);
+  }
+};
 
 __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
     const float* __restrict__ qmean, const float* __restrict__ kmean, const int32_t* __restrict__ bprefix,
@@ -246,12 +278,16 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
   if (h >= H || b >= nb) return;
   const int s = find_segment(bprefix, n_seg, b);
   const int cb0 = bprefix[s];
-  const int n_kb = min(bprefix[s + 1] - cb0, max_blocks);
+  const int n_kb = bprefix[s + 1] - cb0;
   const int tid = threadIdx.x;
   int32_t* out = sel + ((int64_t)h * nb_cap + b) * topk;
 
   if (tid < D) s_q[tid] = qmean[((int64_t)b * H + h) * D + tid] * scale;
   __syncthreads();
+  if (n_kb > max_blocks) {   // longer than the hint: scores recomputed on demand
+    select_topk(ScoredKeys{kmean, cb0, H, h, s_q}, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+    return;
+  }
 
   // scores: one thread per key block, the query mean broadcast from LDS
   uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
@@ -268,7 +304,7 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
     }
     keys[c] = order_key(acc);
   }
-  select_topk(keys, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+  select_topk(LdsKeys{keys}, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,7 +343,8 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
   const int s = find_segment(gprefix, n_seg, g);
   const int cb0 = bprefix[s];
   const int nb_s = bprefix[s + 1] - cb0;
-  const int n_kb = min(nb_s, max_blocks);
+  const int n_kb = nb_s;
+  const bool fits = n_kb <= max_blocks;   // else: longer than the hint, scores recomputed on demand
   const int qb0 = (g - gprefix[s]) * kSelGroup;            // first query block, relative to the segment
   const int nq = min(kSelGroup, nb_s - qb0);
   const int tid = threadIdx.x;
@@ -320,7 +357,7 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
   }
   // thread -> (query j, key row r of the chunk)
   const int j = tid / kSelChunk, r = tid - j * kSelChunk;
-  for (int c0 = 0; c0 < n_kb; c0 += kSelChunk) {
+  for (int c0 = 0; c0 < (fits ? n_kb : 0); c0 += kSelChunk) {
     __syncthreads();   // s_q written / previous chunk consumed
     // 32 rows x 128 floats, 32 lanes per row: 512 contiguous bytes per row
     for (int i = tid; i < kSelChunk * (D / 4); i += kSelThreads) {
@@ -347,7 +384,10 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
   for (int jj = 0; jj < nq; ++jj) {
     __syncthreads();   // keys complete / previous selection's LDS use finished
     int32_t* out = sel + ((int64_t)h * nb_cap + cb0 + qb0 + jj) * topk;
-    select_topk(keys + jj * max_blocks, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+    if (fits)
+      select_topk(LdsKeys{keys + jj * max_blocks}, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
+    else
+      select_topk(ScoredKeys{kmean, cb0, H, h, s_q[jj]}, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
   }
 }
 
@@ -668,6 +708,9 @@ VsaWs carve(void* ws, int64_t total_rows, int64_t n_seg, int64_t H) {
 // Largest per-segment key-block count for the grouped selection: its keys
 // (kSelGroup * max_blocks * 4 bytes) and staging stay within 64 KB of LDS.
 constexpr int kSelGroupMaxBlocks = 1280;
+// Key blocks the one-query-block selection keeps in LDS: 60 KB of keys, so
+// that with its static LDS (2.5 KB) the workgroup stays within 64 KB.
+constexpr int kSelMaxBlocks = 15360;
 
 hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, int n_seg, int max_seqlen,
                              int total_rows, int H, bool bf16, int topk, float scale, int32_t* sel,
@@ -688,7 +731,11 @@ hipError_t launch_vsa_select(const void* q, const void* k, const int32_t* cu, in
                                                                           H, 128, qm, km);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int max_blocks = (int)std::min<int64_t>(ceil_div(std::max(max_seqlen, 1), kVsaBlock), nb_cap);
+  // LDS for the scores, sized from the hint (0: bounded by total_rows); a
+  // longer segment takes the on-demand path, so results do not depend on it
+  const int64_t hint = max_seqlen > 0 ? max_seqlen : std::max(total_rows, 1);
+  const int max_blocks = (int)std::min<int64_t>(std::min<int64_t>(ceil_div(hint, kVsaBlock), nb_cap),
+                                                kSelMaxBlocks);
   if (max_blocks <= kSelGroupMaxBlocks) {
     // groups of kSelGroup query blocks per segment (ceil(L / (64 * kSelGroup)) of them)
     e = launch_build_tiles(cu, n_seg, total_rows, kVsaBlock * kSelGroup, w.gprefix, stream);

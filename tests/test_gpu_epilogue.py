@@ -113,12 +113,14 @@ def test_h3_step_full_size_sampled_rows():
     idxs = h3.unpack_euler(o, perm, torch.from_numpy(wl.tags).to(dev), npm, z, sig, nxt)
     torch.cuda.synchronize()
     tags = wl.tags
+    # indices from the oracle's unpack (a one-element stand-in for the rows:
+    # only the permutation and tags decide them)
+    _, ridx = oracle.unpack(np.zeros((wl.n, 1, 1)), perm.cpu().numpy(), tags)
     rng = np.random.default_rng(9)
     for m in (1, 2):
-        src = np.nonzero(tags == m)[0]
-        assert np.array_equal(idxs[m].cpu().numpy(), src)        # identity packing: idx = source row
+        assert np.array_equal(idxs[m].cpu().numpy(), ridx[m])
+        src = ridx[m].astype(np.int64)                           # packed row of each token of modality m
         ks = np.unique(np.concatenate([[0, 1, len(src) - 1], rng.integers(0, len(src), 48)]))
-        for kk in ks:
-            want = f64(z0[m][kk]) + (nxt[m] - sig[m]) * f64(o[src[kk]])
-            got = f64(z[m][kk])
-            assert np.abs(got - want).max() <= F32_MAX_ABS
+        want = oracle.euler_step(f64(z0[m][ks]), f64(o[src[ks]]), sig[m], nxt[m])
+        max_abs, _ = errors(z[m][ks], want)
+        assert max_abs <= F32_MAX_ABS

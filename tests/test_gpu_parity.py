@@ -83,6 +83,59 @@ def test_many_short_segments(D):
     _check_full(wl, g, r)
 
 
+def test_out_of_range_segment_ids_end_to_end():
+    """Tokens whose segment id is outside 0..n_seg-1 get no packed row: perm is
+    -1 past cu[n_seg] (pre-filled with a stale in-range value here), their
+    per-modality slot keeps idx -1 and an unwritten row, and their Euler state
+    is not stepped; every other output matches the oracle."""
+    wl = W.make_custom([40, 70, 25, 66], H=2, D=128, time_offset=5.0)
+    seg = wl.seg.copy()
+    seg[[3, 50, 51, 130]] = [7, -1, 4, -100]           # four tokens of three modalities dropped
+    wl.seg = seg
+    q, k, v = W.make_qkv(wl, seed=81)
+    d = device_inputs(wl, q, k, v)
+    n, H, D = wl.n, wl.H, wl.D
+    perm = torch.full((n,), 5, dtype=torch.int32, device="cuda")     # stale values
+    mk = lambda: torch.full((wl.capacity, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qp, kp, vp, cu, perm = h3.pack_rope(d["q"], d["k"], d["v"], d["tags"], d["pos"], d["seg"], wl.n_seg,
+                                        wl.rope, wl.time_offset, capacity=wl.capacity, q_out=mk(),
+                                        k_out=mk(), v_out=mk(), perm=perm)
+    r = _oracle_full(wl, q, k, v)
+    total = int(r["cu"][-1])
+    assert total == n - 4
+    assert cu.cpu().numpy().tolist() == r["cu"].tolist()
+    assert perm.cpu().numpy().tolist() == r["perm"].tolist()          # -1 tail included
+    o = mk()
+    h3.varlen_attn_fwd(qp, kp, vp, cu, total_rows=total, max_seqlen=70, o=o)
+    npm = wl.n_per_modality()
+    outs = [torch.full((c, H, D), 3.0, dtype=torch.bfloat16, device="cuda") for c in npm]
+    idxs = [torch.full((c,), 1234, dtype=torch.int32, device="cuda") for c in npm]
+    h3.unpack_by_modality(o, perm, d["tags"], npm, outs=outs, idxs=idxs)
+    torch.cuda.synchronize()
+    assert_close(o[:total], r["o"], "bf16", "O with dropped tokens")
+    for m in range(3):
+        want = r["idxs"][m]
+        assert np.array_equal(idxs[m].cpu().numpy(), want)
+        have = torch.from_numpy(want >= 0).cuda()
+        assert torch.equal(outs[m][have], o[idxs[m][have].long()])
+        assert (outs[m][~have] == 3.0).all()                          # dropped: row not written
+    assert sum(int((x < 0).sum()) for x in r["idxs"]) == 4
+    # the epilogue: dropped tokens keep their state, idx -1
+    z, anchor = W.make_states(wl, seed=82)
+    zd = [x.cuda() for x in z]
+    sig, nxt = (0.0, 0.7, 0.6), (0.0, 0.65, 0.5)
+    idx2 = [torch.full((c,), 1234, dtype=torch.int32, device="cuda") for c in npm]
+    h3.unpack_euler(o, perm, d["tags"], npm, [None, zd[1], zd[2]], sig, nxt, idxs=idx2)
+    torch.cuda.synchronize()
+    new, ridx = oracle.unpack_euler(f64(o[:total]), r["perm"], wl.tags,
+                                    [None, z[1].double().numpy(), z[2].double().numpy()], sig, nxt)
+    for m in (1, 2):
+        assert np.array_equal(idx2[m].cpu().numpy(), ridx[m])
+        assert np.max(np.abs(zd[m].cpu().double().numpy() - new[m])) <= 1e-5
+        dropped = torch.from_numpy(ridx[m] < 0)
+        assert torch.equal(zd[m].cpu()[dropped], z[m][dropped])       # not stepped, bit for bit
+
+
 def test_medium_8527_tokens_full():
     wl = W.make_workload(1)
     q, k, v = W.make_qkv(wl)

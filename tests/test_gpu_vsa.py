@@ -140,7 +140,8 @@ def test_vsa_keep_every_block_equals_dense_attention():
 
 def test_vsa_full_size_cube_grid_sampled():
     # the measured configuration: 59,904 cube-ordered video tokens, 40 heads,
-    # 936 blocks, top-117 (one block in eight)
+    # 936 blocks, top-117 (one block in eight); sampled query blocks of three
+    # heads against the oracle's scores and its block-restricted attention
     wl = W.make_vsa_workload()
     q, k, v = W.make_qkv_on_device(wl, "cuda", seed=5)
     cu = torch.tensor([0, wl.n], dtype=torch.int32, device="cuda")
@@ -152,26 +153,80 @@ def test_vsa_full_size_cube_grid_sampled():
     qs, ks, vs = f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads])
     sel_np = sel[heads].cpu().numpy()
     cu_np = np.array([0, wl.n])
-    # the selection of sampled query blocks against fp64 scores
-    qm, km = oracle.block_means(qs, cu_np), oracle.block_means(ks, cu_np)
+    scores = oracle.vsa_scores(qs, ks, cu_np)[0]             # [3 heads, 936, 936]
     rng = np.random.default_rng(1)
     blocks = np.unique(np.concatenate([[0, 935], rng.integers(0, 936, 10)]))
-    sc = 1 / np.sqrt(128)
     for hi in range(3):
         for b in blocks:
-            row = km[:, hi] @ qm[b, hi] * sc
+            row = scores[hi, b]
             kept = sel_np[hi, b]
             assert len(set(kept.tolist())) == topk and (kept >= 0).all()
             drop = np.setdiff1d(np.arange(936), kept)
             assert row[kept].min() >= row[drop].max() - MARGIN
-            # attention of the block's rows over the kept keys
-            keys = np.concatenate([np.arange(64 * c, 64 * c + 64) for c in kept])
-            S = qs[64 * b:64 * b + 64, hi] @ ks[keys, hi].T * sc
-            P = np.exp(S - S.max(axis=1, keepdims=True))
-            ref = (P / P.sum(axis=1, keepdims=True)) @ vs[keys, hi]
-            got = f64(o[64 * b:64 * b + 64, heads[hi]])
-            assert np.abs(got - ref).max() <= 2e-2
-            assert np.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 5e-3
+    ref = oracle.vsa_attention_blocks(qs, ks, vs, cu_np, sel_np, blocks, heads=[0, 1, 2])
+    for b, rb in zip(blocks, ref):
+        assert_close(o[64 * b:64 * b + 64, heads], rb, "bf16", "VSA O full size, block %d" % b)
+
+
+def test_vsa_selection_does_not_depend_on_the_hint():
+    """max_seqlen only sizes the scores' on-chip buffer: with a hint below a
+    segment's length that segment is scored on demand, which must give the
+    same selection bit for bit, in the grouped kernel (hints up to 1,280
+    blocks) and in the per-block kernel (longer hints; a first segment of
+    1,301 blocks needs one); and it must pass the oracle check."""
+    lengths = [64 * 1300 + 17, 64 * 40, 5]
+    H, topk = 1, 9
+    (q, k, v), cu, rows = _packed(lengths, H, seed=15)
+    dq, dk = q.cuda(), k.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    hints = {"exact": max(lengths), "unknown": 0, "grouped_below": 64 * 1280, "tiny": 1,
+             "per_block_below": 64 * 1290}
+    sels = {name: h3.vsa_select(dq, dk, dcu, rows, topk, max_seqlen=hint) for name, hint in hints.items()}
+    torch.cuda.synchronize()
+    for name, s in sels.items():
+        assert torch.equal(s, sels["exact"]), name
+    nb = oracle.block_layout(cu)[2][-1]
+    assert _check_selection(sels["exact"][:, :nb].cpu().numpy(), W.to_f64(q[:rows]), W.to_f64(k[:rows]), cu,
+                            topk) > 0
+
+
+@pytest.mark.parametrize("rate", [0.3, 0.04])
+def test_vsa_online_softmax_rescale_under_rotated_walks(rate):
+    """Logits that climb along each segment by `rate` (log2 units) per key, so
+    the running max moves and the accumulators are rescaled every one (rate
+    0.3) or every few (0.04) 32-key halves.  24 heads x 43 blocks put about
+    129 items on each XCD, so the walks start at positions spread over the
+    whole segment and wrap around to lower blocks (whose logits then lie far
+    below the reference).  Both the gate's top-k and caller lists of every
+    block are checked against the oracle."""
+    lengths = [64 * 20, 64 * 12 + 20, 64 * 9 + 3]
+    H = 24
+    (q, k, v), cu, rows = _packed(lengths, H, seed=41)
+    amp = 4.0
+    qf, kf = q.float() * 0.1, k.float() * 0.1
+    qf[:, :, 0] += amp
+    ramp = rate / (128 ** -0.5 * np.log2(np.e) * amp)        # k[:, :, 0] step per key
+    for a, b in zip(cu[:-1], cu[1:]):
+        kf[a:b, :, 0] += (torch.arange(b - a, dtype=torch.float32) * ramp)[:, None]
+    q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    _, bseg, bcu = oracle.block_layout(cu)
+    nb = int(bcu[-1])
+    nb_cap = h3.vsa_blocks_bound(rows, len(lengths))
+    every = np.full((H, nb_cap, 20), -1, np.int32)
+    for b in range(nb):
+        s = int(bseg[b])
+        own = np.arange(bcu[s], bcu[s + 1])
+        every[:, b, :len(own)] = own
+    q64, k64, v64 = W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows])
+    sel = h3.vsa_select(dq, dk, dcu, rows, 8, max_seqlen=max(lengths))
+    for lists, topk in ((torch.from_numpy(every).cuda(), 20), (sel, 8)):
+        o = torch.full_like(dq, float("nan"))
+        h3.vsa_attn_fwd(dq, dk, dv, dcu, rows, lists, topk, o=o)
+        torch.cuda.synchronize()
+        ref = oracle.vsa_attention(q64, k64, v64, cu, lists[:, :nb].cpu().numpy())
+        assert_close(o[:rows], ref, "bf16", "VSA rescale rate %g, top-%d" % (rate, topk))
 
 
 def test_vsa_attention_on_caller_lists():

@@ -61,6 +61,33 @@ def test_page_exact_zero_weights(golden):
     assert np.allclose(P.sum(axis=2), 1.0, atol=1e-15, rtol=0)
 
 
+def test_attention_weights_in_block_values():
+    """Inside the segment blocks the weight matrix is the softmax itself: each
+    diagonal block equals torch's float64 softmax of that segment's scaled
+    scores (a library routine), and P.V equals the attention output, which is
+    pinned to torch's scaled_dot_product_attention separately.  A wrong scale,
+    a transposed block or weights taken from the wrong segment fail one of
+    these."""
+    wl = W.make_workload(0)
+    q, k, v = _f64(wl)
+    r = oracle.run(q, k, v, wl.tags, wl.pos, wl.seg, wl.n_seg, wl.rope, wl.time_offset)
+    qp, kp, vp, cu = r["q"], r["k"], r["v"], r["cu"]
+    P = oracle.attention_weights(qp, kp, cu)
+    D = qp.shape[2]
+    for h in range(wl.H):
+        assert np.allclose(P[h] @ vp[:, h], r["o"][:, h], atol=1e-14, rtol=0)
+        for a, b in zip(cu[:-1], cu[1:]):
+            S = torch.from_numpy(qp[a:b, h]) @ torch.from_numpy(kp[a:b, h]).T
+            want = torch.softmax(S * (1.0 / np.sqrt(D)), dim=1).numpy()
+            assert np.allclose(P[h, a:b, a:b], want, atol=1e-15, rtol=0)
+    # a non-default scale moves the weights the same way
+    P2 = oracle.attention_weights(qp, kp, cu, softmax_scale=0.3)
+    a, b = int(cu[1]), int(cu[2])
+    S = torch.from_numpy(qp[a:b, 1]) @ torch.from_numpy(kp[a:b, 1]).T
+    assert np.allclose(P2[1, a:b, a:b], torch.softmax(S * 0.3, dim=1).numpy(), atol=1e-15, rtol=0)
+    assert not np.allclose(P2[1, a:b, a:b], P[1, a:b, a:b], atol=1e-3)
+
+
 def test_page_trim_numbers(golden):
     ex = golden["trim_padding"]
     assert ex["aligned_length"] - ex["effective_tokens"] == ex["padding"]
@@ -114,10 +141,10 @@ def _pack_brute(seg, n_seg):
         members = [i for i in range(len(seg)) if seg[i] == s]
         perm += members
         cu.append(cu[-1] + len(members))
-    return cu, perm
+    return cu, perm + [-1] * (len(seg) - len(perm))
 
 
-@pytest.mark.parametrize("case", ["c4_shifted", "random", "empty_segments"])
+@pytest.mark.parametrize("case", ["c4_shifted", "random", "empty_segments", "dropped", "all_dropped"])
 def test_pack_stable_bruteforce(case):
     rng = np.random.default_rng(7)
     if case == "c4_shifted":
@@ -125,8 +152,12 @@ def test_pack_stable_bruteforce(case):
         seg, n_seg = wl.seg[:6000], wl.n_seg      # a prefix: still unsorted windows
     elif case == "random":
         seg, n_seg = rng.integers(0, 13, size=500).astype(np.int32), 13
-    else:
+    elif case == "empty_segments":
         seg, n_seg = np.array([3, 3, 0, 5, 0, 3], np.int32), 7
+    elif case == "dropped":                       # ids outside 0..n_seg-1 belong to no segment
+        seg, n_seg = np.array([2, -1, 0, 9, 2, 7, 0, -5, 1], np.int32), 7
+    else:
+        seg, n_seg = np.array([4, -1, 4], np.int32), 3
     cu, perm = oracle.pack(seg, n_seg)
     cu_b, perm_b = _pack_brute(seg.tolist(), n_seg)
     assert cu.tolist() == cu_b and perm.tolist() == perm_b
@@ -352,6 +383,33 @@ def test_unpack_bruteforce_and_grid_order():
     assert sorted(np.concatenate(idxs).tolist()) == list(range(n))
 
 
+def test_unpack_and_epilogue_with_dropped_tokens_bruteforce():
+    """Tokens whose segment id is out of range have no packed row: pure-Python
+    loops give their place in the modality slice index -1 and no value, and
+    leave their state unstepped."""
+    seg = np.array([0, 5, 1, -1, 0, 1, 2, 0], np.int32)          # tokens 1 and 3 dropped (n_seg 3)
+    tags = np.array([0, 1, 1, 2, 2, 1, 0, 1], np.uint8)
+    n = seg.shape[0]
+    cu, perm = oracle.pack(seg, 3)
+    assert cu.tolist() == [0, 3, 5, 6] and perm.tolist() == [0, 4, 7, 2, 5, 6, -1, -1]
+    o = np.arange(6, dtype=np.float64)[:, None, None] * 10.0 + 1.0   # packed rows 0..5
+    outs, idxs = oracle.unpack(o, perm, tags)
+    row_of = {int(perm[p]): p for p in range(n) if perm[p] >= 0}
+    for m in range(3):
+        src = [i for i in range(n) if tags[i] == m]
+        assert idxs[m].tolist() == [row_of.get(i, -1) for i in src]
+        for kk, i in enumerate(src):
+            if i in row_of:
+                assert outs[m][kk, 0, 0] == 10.0 * row_of[i] + 1.0
+            else:
+                assert np.isnan(outs[m][kk]).all()
+    z = [None, np.ones((4, 1, 1)), np.full((2, 1, 1), 2.0)]
+    new, _ = oracle.unpack_euler(o, perm, tags, z, (0.0, 0.5, 0.5), (0.0, 0.25, 0.25))
+    # video tokens 1 (dropped), 2, 5, 7 -> rows -, 3, 4, 2;  audio tokens 3 (dropped), 4 -> rows -, 1
+    assert new[1][:, 0, 0].tolist() == [1.0, 1.0 - 0.25 * 31.0, 1.0 - 0.25 * 41.0, 1.0 - 0.25 * 21.0]
+    assert new[2][:, 0, 0].tolist() == [2.0, 2.0 - 0.25 * 11.0]
+
+
 def test_run_end_to_end_tiny():
     wl = W.make_workload(0)
     q, k, v = _f64(wl)
@@ -554,6 +612,19 @@ def test_vsa_attention_matches_masked_sdpa():
             torch.from_numpy(q[:, h])[None], torch.from_numpy(k[:, h])[None], torch.from_numpy(v[:, h])[None],
             attn_mask=mask[None])
         assert np.allclose(got[:, h], ref[0].numpy(), atol=1e-12, rtol=0)
+
+
+def test_vsa_attention_blocks_is_the_restriction():
+    q, k, v = _rand_qkv(333, 4, 8, 9)
+    cu = np.array([0, 50, 50, 333])
+    sel = oracle.vsa_select(q, k, cu, topk=3)
+    full = oracle.vsa_attention(q, k, v, cu, sel)
+    bstart, _, _ = oracle.block_layout(cu)
+    heads = [3, 1]
+    blocks = [0, 2, 5]                                  # a one-block segment, a full block, the short last one
+    got = oracle.vsa_attention_blocks(q, k, v, cu, sel[heads], blocks, heads)
+    for b, ob in zip(blocks, got):
+        assert np.array_equal(ob, full[bstart[b]:bstart[b + 1]][:, heads])
 
 
 def test_vsa_key_permutation_inside_a_kept_block():
