@@ -12,7 +12,9 @@ import os
 from typing import Optional, Sequence, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libh3.so")
+# H3_LIBRARY selects another build of the same library (e.g. the host
+# sanitizer build, `python -m packed_varlen_attention_amd.build --sanitize`).
+LIB_PATH = os.environ.get("H3_LIBRARY") or os.path.join(PKG_DIR, "libh3.so")
 
 H3_BF16, H3_F32 = 0, 1
 TEXT, VIDEO, AUDIO = 0, 1, 2

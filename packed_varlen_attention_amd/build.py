@@ -1,10 +1,16 @@
 """Build libh3.so for gfx950 with hipcc, in-tree.
 
-    python -m packed_varlen_attention_amd.build [--jobs N] [--verbose]
+    python -m packed_varlen_attention_amd.build [--jobs N] [--verbose] [--sanitize]
 
 Each .hip source under csrc/ is compiled to an object under _build/ (in
 parallel), then linked into packed_varlen_attention_amd/libh3.so.  Device code
 is built with packed-fp32 instructions disabled.
+
+--sanitize builds a host-checking variant instead, _build/sanitize/libh3.so:
+the host code (argument validation, workspace carving, launch set-up) with
+AddressSanitizer and UndefinedBehaviorSanitizer, the device code unchanged.
+It is for CPU runs of the host-side tests (load it with H3_LIBRARY=<path> and
+the ASan runtime in LD_PRELOAD); it is never what the GPU runs.
 """
 from __future__ import annotations
 
@@ -38,6 +44,25 @@ COMMON_FLAGS = [
 ]
 
 
+# Host-only sanitizer flags: each -fsanitize applies to the host pass alone.
+SANITIZE_FLAGS = ["-O1", "-g",
+                  "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-shared-libasan"]
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan shared runtime that the sanitizer build links."""
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang ASan runtime not found under %s" % root)
+    return hits[-1]
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -49,9 +74,11 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + ["-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    out_dir = SANITIZE_DIR if sanitize else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    flags = [f for f in COMMON_FLAGS if f != "-O3"] + SANITIZE_FLAGS if sanitize else COMMON_FLAGS
+    cmd = [hipcc()] + flags + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,29 +91,34 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 0, verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir = SANITIZE_DIR if sanitize else BUILD_DIR
+    lib_path = os.path.join(SANITIZE_DIR, "libh3.so") if sanitize else LIB_PATH
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), srcs))
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + \
+        (SANITIZE_LINK if sanitize else []) + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host ASan + UBSan variant under _build/sanitize/ (CPU runs of the host tests only)")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.sanitize))
 
 
 if __name__ == "__main__":

@@ -3,6 +3,7 @@
 // is launched; the library allocates no device memory and keeps no state.
 #include <math.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 #include <vector>
@@ -24,8 +25,18 @@ constexpr int32_t kMaxHeads = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-h3_status check_dims(int32_t H, int32_t D, h3_dtype dt) {
-  if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
+// A C caller may pass any int as h3_dtype; loading a value outside the
+// enumerators' range as the enum type is undefined in C++, so the argument's
+// bits are checked in its slot before the enum value is used anywhere.
+bool dtype_valid(const h3_dtype& dt) {
+  int32_t v;
+  static_assert(sizeof(dt) == sizeof(v), "h3_dtype is int-sized");
+  memcpy(&v, &dt, sizeof v);
+  return v == H3_BF16 || v == H3_F32;
+}
+
+h3_status check_dims(int32_t H, int32_t D, const h3_dtype& dt) {
+  if (!dtype_valid(dt)) return H3_ERR_DTYPE;
   if (H <= 0 || H > kMaxHeads) return H3_ERR_SHAPE;
   if (D != 64 && D != 128) return H3_ERR_UNSUPPORTED;
   return H3_OK;
@@ -56,7 +67,7 @@ h3_status noalloc_scratch(void** out) {
 // Host checks of the attention call that do not involve the workspace.
 // Returns H3_OK with *nothing = true for an empty problem.
 h3_status attn_checks(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_seg,
-                      int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt,
+                      int32_t max_seqlen, int32_t total_rows, int32_t H, int32_t D, const h3_dtype& dt,
                       float softmax_scale, const void* o, bool* nothing) {
   *nothing = false;
   h3_status st = check_dims(H, D, dt);
@@ -89,7 +100,12 @@ h3_status attn_dispatch(const void* q, const void* k, const void* v, const int32
 extern "C" {
 
 const char* h3_status_string(h3_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the bits as int, since loading a value
+  // outside the enumerators' range as h3_status is undefined in C++.
+  int32_t v;
+  static_assert(sizeof(s) == sizeof(v), "h3_status is int-sized");
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case H3_OK: return "ok";
     case H3_ERR_NULL: return "a required pointer is NULL";
     case H3_ERR_DTYPE: return "unknown dtype";
@@ -192,7 +208,7 @@ h3_status h3_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v
 h3_status h3_quantize_qk_fp8(const void* q, const void* k, int32_t rows, int32_t H, int32_t D, h3_dtype dt,
                              float softmax_scale, uint8_t* q8, uint8_t* qe, uint8_t* k8, uint8_t* ke,
                              hipStream_t stream) {
-  if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
+  if (!dtype_valid(dt)) return H3_ERR_DTYPE;
   if (dt != H3_BF16 || D != 128) return H3_ERR_UNSUPPORTED;
   if (H <= 0 || H > kMaxHeads || rows < 0 || rows > kMaxRows) return H3_ERR_SHAPE;
   if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale)) return H3_ERR_UNSUPPORTED;
@@ -209,7 +225,7 @@ h3_status h3_varlen_attn_fwd_fp8qk(const uint8_t* q8, const uint8_t* qe, const u
                                    const void* v, const int32_t* cu_seqlens, int32_t n_seg, int32_t max_seqlen,
                                    int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, void* o,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (dt != H3_BF16 && dt != H3_F32) return H3_ERR_DTYPE;
+  if (!dtype_valid(dt)) return H3_ERR_DTYPE;
   if (dt != H3_BF16 || D != 128) return H3_ERR_UNSUPPORTED;
   if (H <= 0 || H > kMaxHeads) return H3_ERR_SHAPE;
   if (n_seg < 0 || total_rows < 0 || max_seqlen < 0 || total_rows > kMaxRows) return H3_ERR_SHAPE;
@@ -311,7 +327,7 @@ size_t h3_vsa_workspace_bytes(int32_t total_rows, int32_t n_seg, int32_t H) {
 }
 
 namespace {
-h3_status vsa_common_checks(int32_t n_seg, int32_t total_rows, int32_t H, int32_t D, h3_dtype dt, float scale,
+h3_status vsa_common_checks(int32_t n_seg, int32_t total_rows, int32_t H, int32_t D, const h3_dtype& dt, float scale,
                             int32_t topk) {
   h3_status st = check_dims(H, D, dt);
   if (st != H3_OK) return st;
