@@ -77,6 +77,54 @@ __device__ __forceinline__ void exp2_to_bf16(const f32x16_t& sacc, bf16x8_t (&pk
   l_run = lsum;
 }
 
+// Rare path of the lazy online softmax of the bf16 kernels.  `sacc` holds a
+// 32-key half's scores relative to the reference m (log2 units); when any
+// lane's exceed it by more than 2^kRescaleLog2, m moves to the pair's max,
+// O and l are rescaled by 2^-delta, and the pending scores and the -m
+// accumulator-input block are shifted by -delta (exact: numerator and
+// denominator share m).  Otherwise nothing changes (p <= 256).
+//
+// O is multiplied in place by inline-asm v_mul_f32 so that the accumulators
+// keep their registers on both sides of the branch (a plain multiply makes
+// the compiler copy all 64 on the common path).  The compiler's hazard
+// checks do not see into the asm, so the waits are explicit:
+//   * before the multiplies, 24 wait states (3 x s_nop 7): covers the
+//     v_exp_f32 result read (transcendental write -> VALU read) and the last
+//     PV MFMA's writes of O (a 32x32 bf16 MFMA result -> VALU read/write,
+//     the longest such hazard on this part, 18 states);  alpha is routed
+//     through that asm so the exponential is issued before the wait;
+//   * after them, 8 wait states (s_nop 7): VALU write -> MFMA read of the
+//     same VGPRs by the next PV MFMA.
+// The empty volatile asm at the branch head keeps the compiler from
+// if-converting the rescale into an unconditional one on every step.
+__device__ __forceinline__ void lazy_rescale_bf16(f32x16_t& sacc, f32x16_t (&oacc)[4], float& m_run,
+                                                  float& l_run, f32x16_t& neg_m) {
+  const float mloc = lane_max16(sacc);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
+    __asm__ volatile("; rescale" ::: "memory");
+    const float mpair = swap_halves_max(mloc);
+    const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
+    float alpha = __builtin_amdgcn_exp2f(-delta);
+    __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = oacc[db][i];
+        __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+        oacc[db][i] = x;
+      }
+    __asm__ volatile("s_nop 7" ::: "memory");
+    m_run += delta;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] -= delta;
+      neg_m[i] = -m_run;
+    }
+  }
+}
+
 // Byte offsets, within a swizzled 64-key V tile, of the lane's transposing
 // reads: ds_read_b64_tr_b16 at voff[db] (+ 8 rows for the second half of the
 // operand) yields the V^T A operand of output block db (d = 32db .. +31).

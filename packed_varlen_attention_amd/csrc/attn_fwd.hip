@@ -420,43 +420,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_d128_kernel(
       }
     }
   };
-  // Rare path: a half tile's scores exceed the reference by more than 2^8.
-  // Move m to the pair's max, rescale O and l by 2^-delta, and shift the
-  // pending scores (computed against the old m) by -delta.
+  // rare path of the lazy softmax (attn_common.h)
   auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
-    const float mloc = lane_max16(sacc);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
-      // The empty volatile asm keeps the compiler from if-converting this
-      // into an unconditional rescale on every step.
-      __asm__ volatile("; rescale" ::: "memory");
-      const float mpair = swap_halves_max(mloc);
-      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
-      float alpha = __builtin_amdgcn_exp2f(-delta);
-      // The multiplies below are inline asm, which the compiler's hazard
-      // checks do not see: wait out the v_exp_f32 result (transcendental
-      // write -> VALU read) and the last PV MFMA writes of oacc (matrix
-      // result -> VALU read/write) here.  Routing alpha through the asm pins
-      // the exp before the wait.
-      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
-      l_run *= alpha;
-      // In-place multiply: the accumulators keep their registers on both
-      // sides of this branch, so the common path pays no register copies.
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = oacc[db][i];
-          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
-          oacc[db][i] = x;
-        }
-      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
-      m_run += delta;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[i] -= delta;
-        neg_m[i] = -m_run;
-      }
-    }
+    lazy_rescale_bf16(sacc, oacc, m_run, l_run, neg_m);
   };
   auto k_half = [&](int stage, int half) __attribute__((always_inline)) { return k_stage(stage) + half * 8192; };
   auto v_half = [&](int stage, int half) __attribute__((always_inline)) { return v_stage(stage) + half * 8192; };
@@ -746,43 +712,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_short_kernel(
       }
     }
   };
-  // Rare path: a half tile's scores exceed the reference by more than 2^8.
-  // Move m to the pair's max, rescale O and l by 2^-delta, and shift the
-  // pending scores (computed against the old m) by -delta.
+  // rare path of the lazy softmax (attn_common.h)
   auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
-    const float mloc = lane_max16(sacc);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
-      // The empty volatile asm keeps the compiler from if-converting this
-      // into an unconditional rescale on every step.
-      __asm__ volatile("; rescale" ::: "memory");
-      const float mpair = swap_halves_max(mloc);
-      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
-      float alpha = __builtin_amdgcn_exp2f(-delta);
-      // The multiplies below are inline asm, which the compiler's hazard
-      // checks do not see: wait out the v_exp_f32 result (transcendental
-      // write -> VALU read) and the last PV MFMA writes of oacc (matrix
-      // result -> VALU read/write) here.  Routing alpha through the asm pins
-      // the exp before the wait.
-      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
-      l_run *= alpha;
-      // In-place multiply: the accumulators keep their registers on both
-      // sides of this branch, so the common path pays no register copies.
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = oacc[db][i];
-          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
-          oacc[db][i] = x;
-        }
-      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
-      m_run += delta;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[i] -= delta;
-        neg_m[i] = -m_run;
-      }
-    }
+    lazy_rescale_bf16(sacc, oacc, m_run, l_run, neg_m);
   };
 
   // ---- prologue: first half of tile 0; its max sets the reference
@@ -1097,34 +1029,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
       }
     }
   };
-  // Rare path, as in the main kernel: move m by the pair's max when a half
-  // tile's scores exceed the reference by more than 2^8, rescale O and l.
+  // rare path of the lazy softmax (attn_common.h)
   auto update_max = [&](f32x16_t& sacc) __attribute__((always_inline)) {
-    const float mloc = lane_max16(sacc);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0, 0)) {
-      __asm__ volatile("; rescale" ::: "memory");
-      const float mpair = swap_halves_max(mloc);
-      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
-      float alpha = __builtin_amdgcn_exp2f(-delta);
-      // wait states the hazard checks do not see through the asm multiplies
-      __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(alpha) :: "memory");
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = oacc[db][i];
-          __asm__ volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
-          oacc[db][i] = x;
-        }
-      __asm__ volatile("s_nop 7" ::: "memory");   // VALU write -> MFMA read of the same VGPRs
-      m_run += delta;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[i] -= delta;
-        neg_m[i] = -m_run;
-      }
-    }
+    lazy_rescale_bf16(sacc, oacc, m_run, l_run, neg_m);
   };
 
   // ---- prologue: the first two tiles, then the first item's Q
