@@ -858,6 +858,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_short_kernel(
 // bit-identical to it.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMultiItemsPerSlot = 4;    // items per workgroup slot (host bound) that select it
+constexpr int kMultiMaxItems = 512;      // items one workgroup can list in its LDS item table
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -871,6 +872,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
   constexpr int kB = kTileBytes / 2;       // one 32-key K or V tile (8 KB)
   constexpr int NST = 4;                   // ring stages; stage s: K at 2s*kB, V at (2s+1)*kB
   __shared__ __attribute__((aligned(1024))) char ring[NST * 2 * kB];
+  // (head, segment start, segment length, first query row) of this
+  // workgroup's items in visiting order
+  __shared__ int4 item_table[kMultiMaxItems];
 
   // ---- this workgroup's items: w = w_begin, w_begin + stride, ... < w_end
   const int T = prefix[n_seg];             // items per head
@@ -881,6 +885,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
   const int w_begin = xcd * per + (int)(blockIdx.x >> 3);
   const int w_end = min(xcd * per + per, W);
   if (w_begin >= w_end) return;
+  // at most ceil(per / stride) <= kMultiMaxItems: T <= ceil(total_rows / 128) + n_seg,
+  // the host's tile bound, from which it chose this kernel
+  const int n_items = min((w_end - w_begin + stride - 1) / stride, kMultiMaxItems);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
@@ -888,17 +895,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
   const int64_t rs = (int64_t)H * D;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
-  // Item w: head, segment bounds (clamped as the tile counts were) and first query row.
-  struct Item { int h, seg_start, L, q0; };
-  auto item_at = [&](int w) __attribute__((always_inline)) -> Item {
-    Item it;
-    it.h = w / T;
-    const int t = w - it.h * T;
+  // The item table, built once: each lane looks up one item's segment (the
+  // searches run in parallel instead of one dependent scalar chain per item
+  // on the loop's critical path).  Segment bounds are clamped as the tile
+  // counts were.
+  for (int kk = tid; kk < n_items; kk += 256) {
+    const int w = w_begin + kk * stride;
+    const int h = w / T;
+    const int t = w - h * T;
     const int s = find_segment(prefix, n_seg, t);
-    it.seg_start = min(max(cu[s], 0), total_rows);
-    const int seg_end = max(min(cu[s + 1], total_rows), it.seg_start);
-    it.L = seg_end - it.seg_start;
-    it.q0 = it.seg_start + (t - prefix[s]) * kBMs;
+    const int seg_start = min(max(cu[s], 0), total_rows);
+    const int seg_end = max(min(cu[s + 1], total_rows), seg_start);
+    item_table[kk] = make_int4(h, seg_start, seg_end - seg_start, seg_start + (t - prefix[s]) * kBMs);
+  }
+  __syncthreads();
+
+  // Item kk of this workgroup: head, segment bounds and first query row (scalar).
+  struct Item { int h, seg_start, L, q0; };
+  auto item_at = [&](int kk) __attribute__((always_inline)) -> Item {
+    const int4 e = item_table[kk];
+    Item it;
+    it.h = __builtin_amdgcn_readfirstlane(e.x);
+    it.seg_start = __builtin_amdgcn_readfirstlane(e.y);
+    it.L = __builtin_amdgcn_readfirstlane(e.z);
+    it.q0 = __builtin_amdgcn_readfirstlane(e.w);
     return it;
   };
 
@@ -933,18 +953,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
   auto stage_k = [&](int gt) __attribute__((always_inline)) -> char* { return ring + (gt & (NST - 1)) * (2 * kB); };
   auto stage_v = [&](int gt) __attribute__((always_inline)) -> char* { return stage_k(gt) + kB; };
 
-  // Issue cursor: the next tile to load is tile i_tile of item i_w, global tile number g_issue.
-  int i_w = w_begin, i_tile = 0, g_issue = 0;
-  Item i_it = item_at(i_w);
+  // Issue cursor: the next tile to load is tile i_tile of item i_k, global
+  // tile number g_issue; kt / vt point at that tile's first K / V row (the
+  // item's base is formed once per item, each tile adds 32 rows).
+  int i_k = 0, i_tile = 0, g_issue = 0;
+  Item i_it = item_at(0);
+  const uint16_t* kt = k + (int64_t)i_it.seg_start * rs + (int64_t)i_it.h * D;
+  const uint16_t* vt = v + (int64_t)i_it.seg_start * rs + (int64_t)i_it.h * D;
   auto issue_next = [&]() __attribute__((always_inline)) {
-    if (i_w >= w_end) return;
-    const int key0 = i_tile * 32;
-    const uint16_t* kt = k + ((int64_t)i_it.seg_start + key0) * rs + (int64_t)i_it.h * D;
-    const uint16_t* vt = v + ((int64_t)i_it.seg_start + key0) * rs + (int64_t)i_it.h * D;
+    if (i_k >= n_items) return;
     const u32x4_t rk = rsrc_of(kt), rv = rsrc_of(vt);
     const char* kl = stage_k(g_issue);
     const char* vl = stage_v(g_issue);
-    const int last = i_it.L - 1 - key0;    // last valid row of this tile, relative to its first
+    const int last = i_it.L - 1 - i_tile * 32;   // last valid row of this tile, relative to its first
 #pragma unroll
     for (int tt = 0; tt < DMA_INSTR; ++tt) {
       const uint32_t row = (uint32_t)min(drow[tt], last);   // ragged tail: repeat the last row
@@ -954,8 +975,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
     ++g_issue;
     if (++i_tile == (i_it.L + 31) >> 5) {
       i_tile = 0;
-      i_w += stride;
-      if (i_w < w_end) i_it = item_at(i_w);
+      if (++i_k < n_items) {
+        i_it = item_at(i_k);
+        kt = k + (int64_t)i_it.seg_start * rs + (int64_t)i_it.h * D;
+        vt = v + (int64_t)i_it.seg_start * rs + (int64_t)i_it.h * D;
+      }
+    } else {
+      kt += 32 * rs;
+      vt += 32 * rs;
     }
   };
   // s_waitcnt vmcnt: tile gt has landed.  Loads run two tiles ahead (before
@@ -1037,12 +1064,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
   // ---- prologue: the first two tiles, then the first item's Q
 #pragma unroll
   for (int t0 = 0; t0 < NST - 2; ++t0) issue_next();
-  Item it = item_at(w_begin);
+  Item it = item_at(0);
   load_q(it);
   scale_q();
 
   int g_cons = 0;                   // global number of the current item's first tile
-  for (int w = w_begin;;) {
+  for (int kk = 0;;) {
     L = it.L;
     const int nt = (L + 31) >> 5;
 #pragma unroll
@@ -1083,10 +1110,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
       scur = snxt;
     }
     // Q's registers are free: request the next item's rows now
-    const int w_next = w + stride;
+    const int k_next = kk + 1;
     Item nx = it;
-    if (w_next < w_end) {
-      nx = item_at(w_next);
+    if (k_next < n_items) {
+      nx = item_at(k_next);
       load_q(nx);
     }
     const int g_last = g_cons + nt - 1;
@@ -1131,8 +1158,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
       }
     }
     g_cons += nt;
-    w = w_next;
-    if (w >= w_end) break;
+    kk = k_next;
+    if (kk >= n_items) break;
     it = nx;
     scale_q();   // waits for the next item's Q only: the O stores above stay in flight
   }
@@ -1196,7 +1223,9 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
     if (de == hipSuccess) de = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (de != hipSuccess) return de;
     const int64_t slots = 8 * ceil_div(2 * (int64_t)std::max(n_cu, 8), 8);   // two workgroups per CU
-    if (w_max >= kMultiItemsPerSlot * slots && w_max <= 0x7fffffff)
+    // items per workgroup: ceil(ceil(W / 8) / (slots / 8)), W <= w_max
+    const int64_t items_per_wg = ceil_div(ceil_div(w_max, 8), slots / 8);
+    if (w_max >= kMultiItemsPerSlot * slots && w_max <= 0x7fffffff && items_per_wg <= kMultiMaxItems)
       attn_fwd_bf16_d128_multi_kernel<<<(unsigned)slots, 256, 0, stream>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
           static_cast<uint16_t*>(o), cu, prefix, n_seg, H, total_rows, scale_log2);
