@@ -1070,6 +1070,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d128_multi_kernel(
 
   int g_cons = 0;                   // global number of the current item's first tile
   for (int kk = 0;;) {
+    // Two workgroups share each CU; at equal priority the arbiter favours the
+    // older waves, so the first-placed workgroup ran ~20 % faster and the
+    // second finished alone.  Alternating every wave's priority by item
+    // parity gives neither a lasting preference.
+    if (kk & 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     L = it.L;
     const int nt = (L + 31) >> 5;
 #pragma unroll
