@@ -77,6 +77,17 @@ __device__ __forceinline__ void exp2_to_bf16(const f32x16_t& sacc, bf16x8_t (&pk
   l_run = lsum;
 }
 
+// Four O values times 1/l, rounded to bf16 (nearest even) and packed for one
+// 8-byte store.  Built as a bf16 vector so that each adjacent pair becomes a
+// single v_cvt_pk_bf16_f32 (scalar conversions packed with shifts and ORs
+// cost four instructions per pair).
+__device__ __forceinline__ uint2 scale_pack4_bf16(const f32x16_t& o, int i0, float inv) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t b = {(__bf16)(o[i0] * inv), (__bf16)(o[i0 + 1] * inv), (__bf16)(o[i0 + 2] * inv),
+                      (__bf16)(o[i0 + 3] * inv)};
+  return __builtin_bit_cast(uint2, b);
+}
+
 // Rare path of the lazy online softmax of the bf16 kernels.  `sacc` holds a
 // 32-key half's scores relative to the reference m (log2 units); when any
 // lane's exceed it by more than 2^kRescaleLog2, m moves to the pair's max,
@@ -139,7 +150,10 @@ __device__ __forceinline__ void v_tr_offsets(int lane, int (&voff)[4]) {
 }
 
 // O^T += V^T P^T for the 32 keys of one half whose V rows start at vh_l (two
-// transposing reads per V^T operand).
+// transposing reads per V^T operand).  kFirst: the half is the first of its
+// rows, so O starts from the MFMA's zero accumulator input instead of 64
+// zeroed registers (same bits: the products are added to +0 either way).
+template <bool kFirst = false>
 __device__ __forceinline__ void pv_half_tr(const char* vh_l, const int (&voff)[4], const bf16x8_t (&pk)[2],
                                            f32x16_t (&oacc)[4]) {
 #pragma unroll
@@ -150,7 +164,8 @@ __device__ __forceinline__ void pv_half_tr(const char* vh_l, const int (&voff)[4
       const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
       const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], (kFirst && c == 0) ? f32x16_t{} : oacc[db],
+                                                         0, 0, 0);
     }
 }
 

@@ -378,13 +378,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        uint2 st;
-        const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
-        const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
-        const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
-        const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
-        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        const uint2 st = scale_pack4_bf16(oacc[db], a4 * 4, inv);
         const int chunk = (4 * db + a4) ^ (r32 & 15);
         *reinterpret_cast<uint2*>(ot + r32 * 256 + chunk * 16 + g * 8) = st;
       }

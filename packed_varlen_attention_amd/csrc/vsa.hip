@@ -524,12 +524,25 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
     return (cl >= 0 && cl < seg_blocks) ? cl : -1;
   };
 
-  // first valid entry: both its halves are requested before Q is loaded
+  // The first valid entry sets the softmax reference.  Every later entry
+  // outside the segment (possible only in a caller's list) is walked as a
+  // block with no keys: it reads the first valid block's rows, all its
+  // scores are masked, its P is exactly zero and O and l are unchanged.  The
+  // walk then has no inner loops, which would split the accumulators' live
+  // ranges and copy them on every block.
   int i = 0, cl = -1;
   while (i < n_list && (cl = entry_block(i)) < 0) ++i;
-  int kr0 = seg_start + max(cl, 0) * kVsaBlock;
+  const bool any = i < n_list;
+  const int kr_first = seg_start + max(cl, 0) * kVsaBlock;
+  int kr0 = kr_first;
   int len = min(kVsaBlock, seg_end - kr0);
-  if (i < n_list) {
+  // rows and valid length of entry j (j > i)
+  auto entry_rows = [&](int j, int* kr, int* ln) __attribute__((always_inline)) {
+    const int c = entry_block(j);
+    *kr = c >= 0 ? seg_start + c * kVsaBlock : kr_first;
+    *ln = c >= 0 ? min(kVsaBlock, seg_end - *kr) : 0;
+  };
+  if (any) {
     issue_half(kr0, len, Int<0>{});
     issue_half(kr0, len, Int<1>{});
   }
@@ -558,17 +571,15 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   v_tr_offsets(lane, voff);
 
   f32x16_t oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16_t{};
   float m_run = 0.f, l_run = 0.f;
-  f32x16_t neg_m = f32x16_t{};
+  f32x16_t neg_m;
 
-  auto compute_s = [&](const char* kl, f32x16_t& sacc, bool biased) __attribute__((always_inline)) {
+  auto compute_s = [&](const char* kl, f32x16_t& sacc, auto biased) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + koff[kc]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? (biased ? neg_m : f32x16_t{}) : sacc,
-                                                     0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a, qf[kc], kc == 0 ? (decltype(biased)::value ? neg_m : f32x16_t{}) : sacc, 0, 0, 0);
     }
   };
   auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
@@ -580,43 +591,30 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
       }
     }
   };
-  bool first = true;
-  // one 32-key half: S, reference / rescale test, P, O += V P
-  auto half_step = [&](const char* kl, const char* vl, int key_rel) __attribute__((always_inline)) {
+  // one 32-key half: S, reference (first half) or lazy rescale test, P,
+  // O += V P (O = V P for the first half)
+  auto half_step = [&](const char* kl, const char* vl, int key_rel, auto first) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first)::value != 0;
     // scheduling hint: LDS reads interleaved with the MFMAs in small groups
     // (measured 1 % faster, same bits)
     __builtin_amdgcn_iglp_opt(0);
     f32x16_t sacc;
-    compute_s(kl, sacc, !first);
+    compute_s(kl, sacc, Int<kFirst ? 0 : 1>{});
     mask_tail(sacc, key_rel);
-    const float mloc = lane_max16(sacc);
-    if (first) {
+    if constexpr (kFirst) {
       // the first half of the first kept block sets the reference
-      m_run = swap_halves_max(mloc);
+      m_run = swap_halves_max(lane_max16(sacc));
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         sacc[e] -= m_run;
         neg_m[e] = -m_run;
       }
-      first = false;
-    } else if (__builtin_amdgcn_ballot_w64(mloc > kRescaleLog2) != 0) {
-      // rare: scores exceed the reference by more than 2^8
-      const float mpair = swap_halves_max(mloc);
-      const float delta = mpair > kRescaleLog2 ? mpair : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      m_run += delta;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[e] -= delta;
-        neg_m[e] = -m_run;
-      }
+    } else {
+      lazy_rescale_bf16(sacc, oacc, m_run, l_run, neg_m);
     }
     bf16x8_t pk[2];
     exp2_to_bf16(sacc, pk, l_run);
-    pv_half_tr(vl, voff, pk, oacc);
+    pv_half_tr<kFirst>(vl, voff, pk, oacc);
   };
   // Barrier without the workgroup fence of __syncthreads, which would wait
   // for every tile load in flight: this wave's LDS reads complete first; the
@@ -625,16 +623,15 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   auto bar = [&]() __attribute__((always_inline)) {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-
-  while (i < n_list) {
-    int in = i + 1, cln = -1;
-    while (in < n_list && (cln = entry_block(in)) < 0) ++in;
-    const bool more = in < n_list;
-    const int kr0n = seg_start + max(cln, 0) * kVsaBlock;
-    const int lenn = min(kVsaBlock, seg_end - kr0n);
+  // one kept block (entry i): its two halves, with the next entry's halves
+  // requested as the arrays free up
+  auto block = [&](auto first) __attribute__((always_inline)) {
+    const bool more = i + 1 < n_list;
+    int kr0n = kr_first, lenn = 0;
+    if (more) entry_rows(i + 1, &kr0n, &lenn);
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));   // half 0 landed; half 1 may be in flight
     bar();
-    half_step(lk0, lv0, 0);
+    half_step(lk0, lv0, 0, first);
     bar();                                                  // half 0's arrays are free
     if (more) {
       issue_half(kr0n, lenn, Int<0>{});
@@ -643,27 +640,25 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     bar();
-    half_step(lk1, lv1, 32);
+    half_step(lk1, lv1, 32, Int<0>{});
     bar();                                                  // half 1's arrays are free
     if (more) issue_half(kr0n, lenn, Int<1>{});
-    i = in;
+    ++i;
     len = lenn;
+  };
+  if (any) {
+    block(Int<1>{});
+    while (i < n_list) block(Int<0>{});
   }
 
-  if (qrow < q_end && !first) {
+  if (qrow < q_end && any) {
     const float inv = 1.f / swap_halves_sum(l_run);
     uint16_t* op = o + qrow * rs + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        uint2 st;
-        const __bf16 b0 = (__bf16)(oacc[db][a4 * 4 + 0] * inv);
-        const __bf16 b1 = (__bf16)(oacc[db][a4 * 4 + 1] * inv);
-        const __bf16 b2 = (__bf16)(oacc[db][a4 * 4 + 2] * inv);
-        const __bf16 b3 = (__bf16)(oacc[db][a4 * 4 + 3] * inv);
-        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        const uint2 st = scale_pack4_bf16(oacc[db], a4 * 4, inv);
         *reinterpret_cast<uint2*>(op + db * 32 + a4 * 8 + g * 4) = st;
       }
   }
