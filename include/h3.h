@@ -251,7 +251,9 @@ h3_status h3_unpack_by_modality(const void* o, const int32_t* perm, const uint8_
  * b's segment are ignored; a block listed twice counts twice): softmax over
  * those keys only.  The list may be in any order; the kernel visits it from a
  * start that depends on the item's position in the launch (for L2
- * locality), so results are deterministic for a given device.  bf16, D = 128:
+ * locality), so results are deterministic for a given device.  A query block
+ * whose list keeps no block of its own segment has no keys: its rows of o
+ * are not written.  bf16, D = 128:
  * the dense kernel's numerics (Q * scale * log2 e rounded to bf16 once, fp32
  * accumulation and softmax, bf16 P, one RNE rounding of O).  Rows
  * >= total_rows are neither read nor written.

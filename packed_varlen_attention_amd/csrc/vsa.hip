@@ -534,17 +534,18 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   while (i < n_list && (cl = entry_block(i)) < 0) ++i;
   const bool any = i < n_list;
   const int kr_first = seg_start + max(cl, 0) * kVsaBlock;
-  int kr0 = kr_first;
-  int len = min(kVsaBlock, seg_end - kr0);
-  // rows and valid length of entry j (j > i)
-  auto entry_rows = [&](int j, int* kr, int* ln) __attribute__((always_inline)) {
+  const int len_first = min(kVsaBlock, seg_end - kr_first);
+  int len = len_first;              // keys of the block being consumed (0: none)
+  // entry j (j > i): first row and row count to load, keys it contributes
+  auto entry_rows = [&](int j, int* kr, int* ln_load, int* ln_keys) __attribute__((always_inline)) {
     const int c = entry_block(j);
     *kr = c >= 0 ? seg_start + c * kVsaBlock : kr_first;
-    *ln = c >= 0 ? min(kVsaBlock, seg_end - *kr) : 0;
+    *ln_load = c >= 0 ? min(kVsaBlock, seg_end - *kr) : len_first;
+    *ln_keys = c >= 0 ? *ln_load : 0;
   };
   if (any) {
-    issue_half(kr0, len, Int<0>{});
-    issue_half(kr0, len, Int<1>{});
+    issue_half(kr_first, len_first, Int<0>{});
+    issue_half(kr_first, len_first, Int<1>{});
   }
 
   // ---- Q fragment (B operand) times scale * log2(e)
@@ -627,14 +628,14 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   // requested as the arrays free up
   auto block = [&](auto first) __attribute__((always_inline)) {
     const bool more = i + 1 < n_list;
-    int kr0n = kr_first, lenn = 0;
-    if (more) entry_rows(i + 1, &kr0n, &lenn);
+    int kr0n = kr_first, loadn = len_first, lenn = 0;
+    if (more) entry_rows(i + 1, &kr0n, &loadn, &lenn);
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR));   // half 0 landed; half 1 may be in flight
     bar();
     half_step(lk0, lv0, 0, first);
     bar();                                                  // half 0's arrays are free
     if (more) {
-      issue_half(kr0n, lenn, Int<0>{});
+      issue_half(kr0n, loadn, Int<0>{});
       __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_INSTR)); // half 1 landed; the next half 0 may be in flight
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
     bar();
     half_step(lk1, lv1, 32, Int<0>{});
     bar();                                                  // half 1's arrays are free
-    if (more) issue_half(kr0n, lenn, Int<1>{});
+    if (more) issue_half(kr0n, loadn, Int<1>{});
     ++i;
     len = lenn;
   };

@@ -274,3 +274,63 @@ def test_vsa_attention_on_caller_lists():
     torch.cuda.synchronize()
     ref = oracle.vsa_attention(W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows]), cu, ref_sel)
     assert_close(o[:rows], ref, "bf16", "VSA attention on caller-made lists")
+
+
+def test_vsa_attention_out_of_segment_runs_and_keyless_blocks():
+    """Runs of one to three blocks of other segments anywhere in a caller's
+    list (before, between and after its own blocks, so before and after the
+    first own block of any rotated walk), and lists that keep no block of
+    their own segment.  Kept keys: the oracle on the reduced lists; a query
+    block with no kept key has no softmax, and its rows of o keep the value
+    they had (documented: not written)."""
+    lengths = [200, 64, 450, 70]
+    H, topk = 2, 9
+    (q, k, v), cu, rows = _packed(lengths, H, seed=47)
+    _, bseg, bcu = oracle.block_layout(cu)
+    nb = int(bcu[-1])
+    nb_cap = h3.vsa_blocks_bound(rows, len(lengths))
+    rng = np.random.default_rng(11)
+    sel = np.full((H, nb_cap, topk), -1, np.int32)
+    ref_sel = np.full((H, nb, topk), -1, np.int32)
+    keyless = np.zeros((H, nb), bool)
+    for h in range(H):
+        for b in range(nb):
+            s = int(bseg[b])
+            own = np.arange(bcu[s], bcu[s + 1])
+            others = np.setdiff1d(np.arange(nb), own)
+            if rng.random() < 0.2:                       # no block of its own segment
+                lst = [int(c) for c in rng.choice(others, size=int(rng.integers(1, 4)))]
+            else:
+                mine = [int(c) for c in rng.permutation(own)[:int(rng.integers(1, min(len(own), 3) + 1))]]
+                lst = []
+                for c in mine:                           # a run of foreign blocks before each own block
+                    lst += [int(x) for x in rng.choice(others, size=int(rng.integers(0, 3)))]
+                    lst.append(c)
+                lst += [int(x) for x in rng.choice(others, size=int(rng.integers(0, 4)))]
+            lst = lst[:topk]
+            sel[h, b, :len(lst)] = lst
+            kept = [c for c in lst if bcu[s] <= c < bcu[s + 1]]
+            if kept:
+                ref_sel[h, b, :len(kept)] = kept
+            else:
+                keyless[h, b] = True
+                ref_sel[h, b, 0] = int(own[0])           # any block: these rows are not compared
+    assert keyless.any() and (~keyless).any()
+    sentinel = 3.0
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.full_like(dq, sentinel)
+    h3.vsa_attn_fwd(dq, dk, dv, torch.from_numpy(cu).cuda(), rows, torch.from_numpy(sel).cuda(), topk, o=o)
+    torch.cuda.synchronize()
+    got = o[:rows].float().cpu().numpy()
+    ref = oracle.vsa_attention(W.to_f64(q[:rows]), W.to_f64(k[:rows]), W.to_f64(v[:rows]), cu, ref_sel)
+    bstart, _, _ = oracle.block_layout(cu)
+    row_mask = np.zeros((rows, H), bool)                 # (row, head) pairs with kept keys
+    for h in range(H):
+        for b in range(nb):
+            r0, r1 = int(bstart[b]), int(bstart[b + 1])
+            if keyless[h, b]:
+                assert (got[r0:r1, h, :] == sentinel).all(), "keyless query block %d head %d was written" % (b, h)
+            else:
+                row_mask[r0:r1, h] = True
+    assert_close(torch.from_numpy(got[row_mask]), ref[row_mask], "bf16",
+                 "VSA attention with out-of-segment runs")
