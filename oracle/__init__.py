@@ -62,6 +62,10 @@ the re-pin rule; for VSA, keeping every block reduces to the pinned dense
 attention, torch's float64 SDPA with an explicit block mask, brute-force
 block means and a brute-force top-k on tiny inputs, and invariance under
 permuting keys inside a kept block.  No function here is "parity unpinned".
+
+cache.py stores oracle results on disk (off unless H3_ORACLE_CACHE names a
+directory), keyed by the exact input bytes and the oracle's source, so long
+float64 references resume across test runs; it computes nothing itself.
 """
 from .reference import (TEXT, VIDEO, AUDIO, pack, time_shift, rope_angles, apply_rope,
                         attention, attention_rows, attention_weights, unpack, run,

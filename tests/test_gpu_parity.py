@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.cache import cached
 import packed_varlen_attention_amd as h3
 import workloads as W
 from gpu_common import assert_close, device_inputs, f64, run_path, sample_rows
@@ -181,12 +182,12 @@ def _sampled_full_size(index, heads, n_random):
     # attention, end to end: oracle RoPE of every token for the sampled heads
     qh, kh, vh = W.to_f64(q[:, heads]), W.to_f64(k[:, heads]), W.to_f64(v[:, heads])
     qrh, krh = oracle.rope_qk(qh, kh, wl.tags, wl.pos, wl.rope, wl.time_offset)
-    ref = oracle.attention_rows(qrh[perm], krh[perm], vh[perm], cu, rows)
+    ref = cached(oracle.attention_rows, qrh[perm], krh[perm], vh[perm], cu, rows)
     got = g["o"][rows_d][:, heads]
     assert_close(got, ref, "bf16", "O end-to-end sampled rows")
     # attention, stage-wise on the GPU's own packed tensors
-    ref2 = oracle.attention_rows(f64(g["q"][:n, heads]), f64(g["k"][:n, heads]), f64(g["v"][:n, heads]),
-                                 cu, rows)
+    ref2 = cached(oracle.attention_rows, f64(g["q"][:n, heads]), f64(g["k"][:n, heads]),
+                  f64(g["v"][:n, heads]), cu, rows)
     assert_close(got, ref2, "bf16", "O stage-wise sampled rows")
     # unpack: indices bit-exact, values an exact gather, pad rows untouched
     _, idxs = oracle.unpack(np.zeros((n, 1, 1)), perm, wl.tags)

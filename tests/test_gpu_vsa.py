@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.cache import cached
 import packed_varlen_attention_amd as h3
 import workloads as W
 from gpu_common import F32_MAX_ABS, assert_close, errors, f64
@@ -163,7 +164,7 @@ def test_vsa_full_size_cube_grid_sampled():
             assert len(set(kept.tolist())) == topk and (kept >= 0).all()
             drop = np.setdiff1d(np.arange(936), kept)
             assert row[kept].min() >= row[drop].max() - MARGIN
-    ref = oracle.vsa_attention_blocks(qs, ks, vs, cu_np, sel_np, blocks, heads=[0, 1, 2])
+    ref = cached(oracle.vsa_attention_blocks, qs, ks, vs, cu_np, sel_np, blocks, heads=[0, 1, 2])
     for b, rb in zip(blocks, ref):
         assert_close(o[64 * b:64 * b + 64, heads], rb, "bf16", "VSA O full size, block %d" % b)
 
