@@ -230,6 +230,22 @@ __device__ __forceinline__ void select_topk(const KeyAt& key_at, int n_kb, int t
   for (int i = need_total + tid; i < topk; i += kSelThreads) out[i] = -1;
 }
 
+// The score of a key-block mean against a scaled query mean: four partial
+// sums of fmaf, one per dimension class d mod 4 (each a chain of 32 rather
+// than one chain of 128, which bounded the scoring by its latency),
+// combined as (s0 + s1) + (s2 + s3).  Every scoring site uses this order,
+// so all of them give identical keys.
+struct Score4 {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  __device__ __forceinline__ void add(const float4 x, const float4 y) {
+    s0 = fmaf(x.x, y.x, s0);
+    s1 = fmaf(x.y, y.y, s1);
+    s2 = fmaf(x.z, y.z, s2);
+    s3 = fmaf(x.w, y.w, s3);
+  }
+  __device__ __forceinline__ float sum() const { return (s0 + s1) + (s2 + s3); }
+};
+
 // Keys already scored into LDS.
 struct LdsKeys {
   const uint32_t* keys;
@@ -238,9 +254,9 @@ struct LdsKeys {
 
 // Keys scored on demand, for a segment whose key blocks do not fit the LDS
 // the launch sized from the max_seqlen hint: key c is the score of key block
-// cb0 + c against the scaled query mean sq (in LDS), with the fmaf order of
-// the LDS path, so both give identical keys (the radix select reads every key
-// five times, each time recomputed).
+// cb0 + c against the scaled query mean sq (in LDS, 16-byte aligned), with
+// the summation order of the LDS path (Score4), so both give identical keys
+// (the radix select reads every key five times, each time recomputed).
 struct ScoredKeys {
   const float* kmean;
   int64_t cb0;
@@ -248,16 +264,11 @@ struct ScoredKeys {
   const float* sq;
   __device__ uint32_t operator()(int c) const {
     const float4* km = reinterpret_cast<const float4*>(kmean + ((cb0 + c) * H + h) * 128);
-    float acc = 0.f;
+    const float4* q4 = reinterpret_cast<const float4*>(sq);
+    Score4 sc;
 #pragma unroll 8
-    for (int d4 = 0; d4 < 32; ++d4) {
-      const float4 x = km[d4];
-      acc = fmaf(x.x, sq[4 * d4], acc);
-      acc = fmaf(x.y, sq[4 * d4 + 1], acc);
-      acc = fmaf(x.z, sq[4 * d4 + 2], acc);
-      acc = fmaf(x.w, sq[4 * d4 + 3], acc);
-    }
-    return order_key(acc);
+    for (int d4 = 0; d4 < 32; ++d4) sc.add(km[d4], q4[d4]);
+    return order_key(sc.sum());
   }
 };
 
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
     int n_seg, int H, int nb_cap, int max_blocks, int topk, float scale, int32_t* __restrict__ sel) {
   constexpr int D = 128;
   extern __shared__ float lds_f[];   // scores [max_blocks] then keys as uint32 (aliased)
-  __shared__ float s_q[D];
+  __shared__ __attribute__((aligned(16))) float s_q[D];
   __shared__ int s_hist[256];
   __shared__ int s_scan[kSelThreads];
   __shared__ uint32_t s_prefix;
@@ -293,16 +304,11 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
   uint32_t* keys = reinterpret_cast<uint32_t*>(lds_f);
   for (int c = tid; c < n_kb; c += kSelThreads) {
     const float4* km = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c) * H + h) * D);
-    float acc = 0.f;
+    const float4* q4 = reinterpret_cast<const float4*>(s_q);
+    Score4 sc;
 #pragma unroll 8
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 x = km[d4];
-      acc = fmaf(x.x, s_q[4 * d4], acc);
-      acc = fmaf(x.y, s_q[4 * d4 + 1], acc);
-      acc = fmaf(x.z, s_q[4 * d4 + 2], acc);
-      acc = fmaf(x.w, s_q[4 * d4 + 3], acc);
-    }
-    keys[c] = order_key(acc);
+    for (int d4 = 0; d4 < D / 4; ++d4) sc.add(km[d4], q4[d4]);
+    keys[c] = order_key(sc.sum());
   }
   select_topk(LdsKeys{keys}, n_kb, topk, cb0, out, s_hist, s_scan, s_prefix, s_need);
 }
@@ -315,8 +321,8 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(
 // g indexing groups of kSelGroup consecutive query blocks of a segment
 // (gprefix: exclusive prefix of ceil(blocks / kSelGroup) per segment);
 // workgroups past gprefix[n_seg] exit.  Key means go through LDS 32 rows at a
-// time with coalesced loads; each score is the same fmaf sequence over d as
-// in vsa_select_kernel, so scores and selections are bit-identical to it.
+// time with coalesced loads; each score is summed in the same order as in
+// vsa_select_kernel (Score4), so scores and selections are bit-identical to it.
 // Dynamic LDS: kSelGroup * max_blocks keys.
 // ---------------------------------------------------------------------------
 constexpr int kSelGroup = 8;       // query blocks per workgroup
@@ -368,17 +374,11 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
     }
     __syncthreads();
     if (j < nq && c0 + r < n_kb) {
-      float acc = 0.f;
+      Score4 sc;
 #pragma unroll 8
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 x = *reinterpret_cast<const float4*>(&s_k[r][4 * d4]);
-        const float4 y = *reinterpret_cast<const float4*>(&s_q[j][4 * d4]);
-        acc = fmaf(x.x, y.x, acc);
-        acc = fmaf(x.y, y.y, acc);
-        acc = fmaf(x.z, y.z, acc);
-        acc = fmaf(x.w, y.w, acc);
-      }
-      keys[j * max_blocks + c0 + r] = order_key(acc);
+      for (int d4 = 0; d4 < D / 4; ++d4)
+        sc.add(*reinterpret_cast<const float4*>(&s_k[r][4 * d4]), *reinterpret_cast<const float4*>(&s_q[j][4 * d4]));
+      keys[j * max_blocks + c0 + r] = order_key(sc.sum());
     }
   }
   for (int jj = 0; jj < nq; ++jj) {
