@@ -583,8 +583,12 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
           a, qf[kc], kc == 0 ? (decltype(biased)::value ? neg_m : f32x16_t{}) : sacc, 0, 0, 0);
     }
   };
+  // keys past the block's end (a segment's last, ragged block, or a block
+  // without keys) get -inf; a branch, so full blocks pay no compare-and-select
+  // per score
   auto mask_tail = [&](f32x16_t& sacc, int key_rel) __attribute__((always_inline)) {
-    if (key_rel + 32 > len) {
+    if (__builtin_expect(key_rel + 32 > len, 0)) {
+      __asm__ volatile("; ragged or key-less block" ::: "memory");   // keep it a branch, not selects
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = key_rel + 8 * (e >> 2) + 4 * g + (e & 3);
