@@ -459,23 +459,40 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
   const uint32_t voff_dma = (uint32_t)lrow * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
   const uint16_t* kh = k + (int64_t)h * D;
   const uint16_t* vh = v + (int64_t)h * D;
+  // The loads are inline asm: the compiler's wait-count pass does not see
+  // them, so it cannot add waits for them (it cannot tell the two halves'
+  // arrays apart across the walk's back-edge and would wait for the other
+  // half's loads before reading this half); every wait on them is explicit.
+  // m0 holds the LDS destination of a load-to-LDS instruction; the asm sets it
+  // before every load and nothing else in this kernel uses m0.
+  typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+  auto rsrc_of = [&](const uint16_t* base) __attribute__((always_inline)) -> u32x4v_t {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4v_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                    64u * row_bytes, (uint32_t)kBufferWord3};
+  };
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  auto dma = [&](const u32x4v_t& rsrc, const char* lds, uint32_t voffset, uint32_t soffset) __attribute__((always_inline)) {
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+  };
+#pragma clang diagnostic pop
   auto issue_half = [&](int kr0, int len, auto half_c) __attribute__((always_inline)) {
     constexpr int half = decltype(half_c)::value;
     char* dk = half ? lk1 : lk0;
     char* dv = half ? lv1 : lv0;
-    const int nrec = (int)(64u * row_bytes);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vh + (int64_t)kr0 * rs), (short)0, nrec, kBufferWord3);
+    const u32x4v_t rk = rsrc_of(kh + (int64_t)kr0 * rs);
+    const u32x4v_t rv = rsrc_of(vh + (int64_t)kr0 * rs);
     if (__builtin_expect(len == kVsaBlock, 1)) {
 #pragma unroll
       for (int tt = 0; tt < DMA_INSTR; ++tt) {
         const int row0 = 32 * half + HALF_ROWS * wave + 4 * tt;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + (HALF_ROWS * wave + 4 * tt) * 256), 16,
-                                                 koff_dma[tt], (int)(row0 * row_bytes), 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + (HALF_ROWS * wave + 4 * tt) * 256), 16,
-                                                 voff_dma, (int)(row0 * row_bytes), 0, 0);
+        const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(row0 * row_bytes));
+        dma(rk, dk + (HALF_ROWS * wave + 4 * tt) * 256, koff_dma[tt], so);
+        dma(rv, dv + (HALF_ROWS * wave + 4 * tt) * 256, voff_dma, so);
       }
     } else {
 #pragma unroll
@@ -484,10 +501,8 @@ __global__ __launch_bounds__(128, 2) void vsa_attn_kernel(
         const uint32_t row = (uint32_t)min(32 * half + HALF_ROWS * wave + 4 * tt + lrow, len - 1);
         const uint32_t kc = (uint32_t)(((lane & 15) ^ swz_k(4 * tt + lrow)) << 4);
         const uint32_t vc = (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + (HALF_ROWS * wave + 4 * tt) * 256), 16,
-                                                 row * row_bytes + kc, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + (HALF_ROWS * wave + 4 * tt) * 256), 16,
-                                                 row * row_bytes + vc, 0, 0, 0);
+        dma(rk, dk + (HALF_ROWS * wave + 4 * tt) * 256, row * row_bytes + kc, 0u);
+        dma(rv, dv + (HALF_ROWS * wave + 4 * tt) * 256, row * row_bytes + vc, 0u);
       }
     }
   };
