@@ -149,24 +149,23 @@ __device__ __forceinline__ void v_tr_offsets(int lane, int (&voff)[4]) {
     voff[db] = rl * 256 + ((((4 * db) ^ (sv & 12)) | (cl ^ (sv & 3))) << 4) + (lane & 1) * 8;
 }
 
-// O^T += V^T P^T for the 32 keys of one half whose V rows start at vh_l (two
-// transposing reads per V^T operand).  kFirst: the half is the first of its
-// rows, so O starts from the MFMA's zero accumulator input instead of 64
-// zeroed registers (same bits: the products are added to +0 either way).
-template <bool kFirst = false>
+// The V^T A operand of output block db (d = 32db .. +31) for keys 16c .. +15
+// of a 32-key half whose V rows start at vh_l: two transposing reads.
+__device__ __forceinline__ bf16x8_t v_operand_tr(const char* vh_l, const int (&voff)[4], int db, int c) {
+  const char* vp = vh_l + voff[db] + (16 * c) * 256;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// O^T += V^T P^T for the 32 keys of one half whose V rows start at vh_l.
 __device__ __forceinline__ void pv_half_tr(const char* vh_l, const int (&voff)[4], const bf16x8_t (&pk)[2],
                                            f32x16_t (&oacc)[4]) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const char* vp = vh_l + voff[db] + (16 * c) * 256;
-      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp));
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vp + 8 * 256));
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], (kFirst && c == 0) ? f32x16_t{} : oacc[db],
-                                                         0, 0, 0);
-    }
+    for (int c = 0; c < 2; ++c)
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_tr(vh_l, voff, db, c), pk[c], oacc[db], 0, 0, 0);
 }
 
 }  // namespace
