@@ -363,16 +363,32 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_group_kernel(
   }
   // thread -> (query j, key row r of the chunk)
   const int j = tid / kSelChunk, r = tid - j * kSelChunk;
+  // Key-mean chunks: 32 rows x 128 floats, 32 lanes per row (512 contiguous
+  // bytes per row), PER float4 per thread; the next chunk is loaded into
+  // registers while the current one is scored.
+  constexpr int PER = kSelChunk * (D / 4) / kSelThreads;
+  static_assert(PER * kSelThreads == kSelChunk * (D / 4), "whole float4 per thread");
+  float4 pf[PER];
+  auto load_chunk = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelThreads;
+      const int rr = i / (D / 4), d4 = i - rr * (D / 4);
+      pf[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + rr < n_kb) pf[u] = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c0 + rr) * H + h) * D)[d4];
+    }
+  };
+  if (fits) load_chunk(0);
   for (int c0 = 0; c0 < (fits ? n_kb : 0); c0 += kSelChunk) {
     __syncthreads();   // s_q written / previous chunk consumed
-    // 32 rows x 128 floats, 32 lanes per row: 512 contiguous bytes per row
-    for (int i = tid; i < kSelChunk * (D / 4); i += kSelThreads) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelThreads;
       const int rr = i / (D / 4), d4 = i - rr * (D / 4);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + rr < n_kb) x = reinterpret_cast<const float4*>(kmean + ((int64_t)(cb0 + c0 + rr) * H + h) * D)[d4];
-      *reinterpret_cast<float4*>(&s_k[rr][4 * d4]) = x;
+      *reinterpret_cast<float4*>(&s_k[rr][4 * d4]) = pf[u];
     }
     __syncthreads();
+    if (c0 + kSelChunk < n_kb) load_chunk(c0 + kSelChunk);
     if (j < nq && c0 + r < n_kb) {
       Score4 sc;
 #pragma unroll 8
