@@ -108,22 +108,30 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 // Block-wide exclusive scan of one int per thread (kSelThreads threads);
-// returns the prefix and writes the total to *total.  Uses `buf`
-// (kSelThreads ints of LDS); ends with a barrier.
+// returns the prefix and writes the total to *total.  Each wave scans its 64
+// values with lane shifts, the wave totals meet in `buf` (one int per wave
+// of LDS): two barriers in all; ends with a barrier.
 __device__ int block_excl_scan(int x, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const int y = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += y;
-    __syncthreads();
+  constexpr int kWaves = kSelThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  const int incl = buf[tid];
-  *total = buf[kSelThreads - 1];
+  if (lane == 63) buf[wave] = incl;
   __syncthreads();
-  return incl - x;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = buf[w];
+    before += w < wave ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  __syncthreads();   // buf may be rewritten by the next scan
+  return before + incl - x;
 }
 
 // Top-k of one query block's keys (order_key of its scores, one per key
