@@ -12,24 +12,29 @@
 //   * every (head, query block) keeps the top-k key blocks of its segment,
 //     larger score first, equal scores by lower block index.
 //
-// Three kernels:
+// Kernels:
 //   1. vsa_pool_kernel: fp32 means of the Q and K rows of every block
 //      (one pass over Q and K, HBM-bound);
-//   2. vsa_select_kernel: one workgroup per (head, query block) scores all
-//      key blocks of the segment into LDS (one lane per key block, the query
-//      mean broadcast from LDS) and picks the top-k with a 4-pass 8-bit radix
-//      select on order-preserving keys, then an ordered compaction, so the
-//      list comes out in increasing block order;
+//   2. selection: scores of every key block of the segment against each
+//      query block, then the top-k with a 4-pass 8-bit radix select on
+//      order-preserving keys and an ordered compaction, so each list comes
+//      out in increasing block order.  vsa_select_group_kernel serves 8
+//      query blocks per workgroup (the key means pass through LDS once per
+//      group, the next chunk prefetched into registers);
+//      vsa_select_kernel, one workgroup per query block, serves segments too
+//      long for the grouped kernel's LDS.  Both sum each score in the same
+//      order, so their selections are identical;
 //   3. vsa_attn_kernel: one workgroup of 2 waves per (head, query block),
 //      32 query rows per wave; every kept block's K and V (64 keys x 256 B)
-//      goes HBM -> LDS by direct loads, in two 32-key halves double-buffered
-//      in 32 KB, and is consumed with the dense kernel's operand layout (Q
-//      pre-scaled by scale * log2 e in registers, S^T = K Q^T on 32x32x16
-//      bf16 MFMA with -m folded into the accumulator input, transposed V
-//      reads, bf16 P).  Four workgroups share a CU (LDS 32 KB, 256 VGPRs
-//      each).  Each item walks its kept blocks from a start position that
-//      keeps the workgroups resident on one XCD on neighbouring key blocks,
-//      so the XCD's L2 serves most of them (described above the kernel).
+//      goes HBM -> LDS by direct loads (inline asm, explicit waits), in two
+//      32-key halves double-buffered in 32 KB, and is consumed with the
+//      dense kernel's operand layout (Q pre-scaled by scale * log2 e in
+//      registers, S^T = K Q^T on 32x32x16 bf16 MFMA with -m folded into the
+//      accumulator input, transposed V reads, bf16 P).  Four workgroups share
+//      a CU (LDS 32 KB each, at most 256 VGPRs per wave).  Each item walks
+//      its kept blocks from a start position that keeps the workgroups
+//      resident on one XCD on neighbouring key blocks, so the XCD's L2
+//      serves most of them (described above the kernel).
 #include "attn_common.h"
 
 namespace h3 {
