@@ -1,7 +1,9 @@
 // Device definitions shared by the attention kernels of libh3.so (dense
-// varlen attention in attn_fwd.hip, block-sparse attention in vsa.hip):
-// operand vector types, the swizzled 64-key K/V tile layout in LDS and
-// the exchange between the two lanes that hold one query's S^T column.
+// varlen attention in attn_fwd.hip, FP8 Q.K attention in attn_fp8.hip,
+// block-sparse attention in vsa.hip): operand vector types, the swizzled
+// 64-key K/V tile layout in LDS, the exchange between the two lanes that
+// hold one query's S^T column, the exponentials and row sums of P, the lazy
+// rescale, and the transposed V operand reads of the P.V product.
 #pragma once
 
 #include "h3_internal.h"
