@@ -14,7 +14,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -61,9 +60,32 @@ __device__ __forceinline__ float lane_max16(const f32x16_t& s) {
 }
 
 // P = exp2(S) for one 32-key half (S already relative to the reference), as
-// the two bf16 B operands of the P.V product; l gains the row sum of that
-// bf16 P (v_dot2c_f32_bf16 against ones), the P the product actually uses.
+// the two bf16 B operands of the P.V product; l gains the row sum of the
+// fp32 P, in two interleaved chains of plain adds.  (A sum of the bf16 P by
+// v_dot2c_f32_bf16 against ones overlaps the matrix cores' work poorly on
+// gfx950; the two sums differ by the bf16 rounding of P, far inside the
+// tolerances, and every kernel uses this one helper, so they stay identical
+// to each other.)
 __device__ __forceinline__ void exp2_to_bf16(const f32x16_t& sacc, bf16x8_t (&pk)[2], float& l_run) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sacc[c * 8 + e]);
+      pk[c][e] = (__bf16)p;
+      if (e & 1) s1 += p;
+      else s0 += p;
+    }
+  }
+  l_run += s0 + s1;
+}
+
+// The same P, with l gaining the row sum of the bf16 P by v_dot2c_f32_bf16
+// against ones (8 instructions instead of 16 adds): for the FP8 kernel, whose
+// vector ALU carries more work per MFMA cycle, the fewer instructions win.
+__device__ __forceinline__ void exp2_to_bf16_dotsum(const f32x16_t& sacc, bf16x8_t (&pk)[2], float& l_run) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   float lsum = l_run;
 #pragma unroll

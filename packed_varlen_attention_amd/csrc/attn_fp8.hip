@@ -322,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
       __attribute__((always_inline)) {
     bf16x8_t pk[2];
     f32x16_t snxt;
-    exp2_to_bf16(scur, pk, l_run);
+    exp2_to_bf16_dotsum(scur, pk, l_run);
     compute_s(k_st, k_half, snxt, true);
     pv_half(v_st, v_half, pk);
     if constexpr (decltype(ragged)::value != 0) mask_tail(snxt, key_next);
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8qk_d128_kernel(
   };
   auto final_step = [&](int v_st, int v_half) __attribute__((always_inline)) {
     bf16x8_t pk[2];
-    exp2_to_bf16(scur, pk, l_run);
+    exp2_to_bf16_dotsum(scur, pk, l_run);
     pv_half(v_st, v_half, pk);
   };
   auto tile = [&](auto phase, int j, auto steady) __attribute__((always_inline)) {

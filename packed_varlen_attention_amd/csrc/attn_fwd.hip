@@ -260,8 +260,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 //     by more than 2^8 (exact: numerator and denominator share m; p stays
 //     <= 256 otherwise).  The test is lane-local (each lane's 16 scores
 //     against 8), the exchange between the two lanes of a query only on the
-//     rare rescale.  Row sums use v_dot2c_f32_bf16 over the bf16 P that the
-//     PV product actually uses.
+//     rare rescale.  Row sums add the fp32 P in two chains of plain adds
+//     (a v_dot2c_f32_bf16 sum of the bf16 P overlaps the MFMAs poorly).
 // ---------------------------------------------------------------------------
 constexpr int kBM2 = 256;                 // query rows per workgroup
 constexpr int kStages = 4;                // ring stages (tiles requested kStages-2 ahead)
